@@ -1,0 +1,216 @@
+#!/usr/bin/env python3
+"""Benchmark of the CEM plan step on one MI355X.
+
+Workload: the V-JEPA2-AC-shaped predictor (24 layers, d 1024, 16 heads, MLP 4096,
+256 patch tokens, encoder width 1408, horizon 1) under the search settings of
+page "Real-Time Inference for JEPA World Model Architectures with Ray"
+(section 01: 800 candidates, best 80 kept, 10 rounds).  Random-init weights and
+N(0, 1) embeddings from fixed seeds (the pages ship neither weights nor frames).
+
+One step = one full cem_plan call (sample, rollout, L1 energy, top-K, refit for
+all 10 rounds), inputs resident in HBM.  Prints ONE JSON line:
+  value       = candidate evaluations per second = N * R / plan time
+  ms_per_step = milliseconds per plan step (graph replay)
+  roofline    = the dense-GEMM kernel (the dominant kernel), useful FLOPs over
+                its HIP-event-timed launch durations, against bf16 dense MFMA peak
+  cpu_baseline= the oracle (NumPy float64) on the host cores, on a bounded
+                sample of candidates, extrapolated to the metric's unit
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
+MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (reference for fp32 models)
+
+
+def eprint(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, sample_seconds: float):
+    """Time the oracle on the host: whole candidates through the predictor + energy,
+    then the per-round search bookkeeping, extrapolated to candidate-evals/s."""
+    import numpy as np
+
+    from cem_jepa_predictor_amd import inputs
+    from oracle import energy as o_energy
+    from oracle import predictor as o_pred
+    from oracle import refit as o_refit
+    from oracle import sampler as o_sampler
+    from oracle import select as o_select
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    m, pc = wl.model, wl.plan
+    w = inputs.make_weights(m, wl.weight_seed)
+    z_obs, z_goal, s0 = inputs.make_embeddings(m, wl.embed_seed)
+    pred = o_pred.Predictor(w, m.layers, m.heads, m.ln_eps)
+    del w
+    mu = np.zeros((pc.horizon, m.action_dim), np.float32)
+    sg = np.ones_like(mu)
+    x = o_sampler.sample_actions(mu, sg, pc.seed, 0, pc.plan_id, pc.n_samples, pc.clamp_lo, pc.clamp_hi)
+    done, t0 = 0, time.perf_counter()
+    while done < 64:
+        o_energy.energy_l1(pred.rollout_cached(x[done:done + 1], z_obs, s0), z_goal)
+        done += 1
+        if time.perf_counter() - t0 >= sample_seconds:
+            break
+    t_eval = time.perf_counter() - t0
+    evals_per_s = done / t_eval
+    # search bookkeeping of one full plan (sample + select + refit for every round)
+    t1 = time.perf_counter()
+    e = np.random.default_rng(0).standard_normal(pc.n_samples)
+    for r in range(pc.rounds):
+        xr = o_sampler.sample_actions(mu, sg, pc.seed, r, pc.plan_id, pc.n_samples, pc.clamp_lo, pc.clamp_hi)
+        el = o_select.topk_elites(e, pc.n_elites)
+        o_refit.refit(xr, el)
+    t_book = time.perf_counter() - t1
+    plan_s = pc.n_samples * pc.rounds / evals_per_s + t_book
+    return {"value": round(evals_per_s, 6), "unit": "candidate-evals/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": (f"{done} candidate rollouts + L1 energies of the {wl.name} workload in "
+                       f"{t_eval:.1f} s (NumPy float64), plus one plan's sampling/top-K/refit "
+                       f"({t_book * 1e3:.1f} ms); extrapolated plan step {plan_s:.0f} s")}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="vjepa2ac")
+    ap.add_argument("--samples", type=int, default=0, help="override N (sweep); K = N / 10")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timers", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        eprint("bench.py measures one GPU: the plan step runs on a single MI355X; "
+               "multi-GPU runs are not part of this build (--gpus must be 1).")
+        return 2
+
+    import numpy as np
+    import torch
+
+    from cem_jepa_predictor_amd import _lib, inputs
+
+    if not torch.cuda.is_available():
+        eprint("no GPU available")
+        return 1
+    torch.cuda.set_device(0)
+    if args.samples:
+        wl = inputs.sweep_workload(args.samples)
+    else:
+        wl = inputs.WORKLOADS[args.workload]
+    m, pc = wl.model, wl.plan
+    N, K, R, H, A = pc.n_samples, pc.n_elites, pc.rounds, pc.horizon, m.action_dim
+    eprint(f"[bench] workload {wl.name}: N={N} K={K} R={R} H={H} L={m.layers} d={m.d_model} "
+           f"dtype={m.dtype}")
+    t0 = time.perf_counter()
+    w = inputs.make_weights(m, wl.weight_seed)
+    flat = inputs.flatten_weights(m, w)
+    del w
+    z_obs, z_goal, s0 = inputs.make_embeddings(m, wl.embed_seed)
+    model = _lib.Model(m, flat, N)
+    del flat
+    eprint(f"[bench] model ready in {time.perf_counter() - t0:.1f} s")
+
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
+    zo, zg, st = dev(z_obs), dev(z_goal), dev(s0)
+    mu0 = torch.full((H, A), pc.mu0, device="cuda")
+    sg0 = torch.full((H, A), pc.sigma0, device="cuda")
+    mu, sg = mu0.clone(), sg0.clone()
+    action = torch.empty(A, device="cuda")
+    best = torch.empty(1, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(i: int, use_graph: bool = True):
+        mu.copy_(mu0)
+        sg.copy_(sg0)
+        model.plan(zo, zg, st, mu, sg, action, best, n_samples=N, n_elites=K, rounds=R, horizon=H,
+                   seed=pc.seed, plan_id=i, clamp_lo=pc.clamp_lo, clamp_hi=pc.clamp_hi,
+                   use_graph=use_graph, stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+        torch.cuda.synchronize()
+        eprint(f"[bench] warmup {i + 1}/{args.warmup} done")
+
+    # ---- timed region: K plan steps replayed from the captured graph
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(1000 + i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    eprint(f"[bench] timed {args.steps} steps: {ms:.2f} ms/step (wall {wall:.2f} s)")
+
+    # ---- kernel timers: the same K steps enqueued directly with HIP events around
+    # every dense-GEMM launch, on the stream the kernels run on
+    roof = None
+    eager_ms = None
+    if not args.no_kernel_timers:
+        model.timer_enable(True)
+        torch.cuda.synchronize()
+        ev0.record(stream)
+        for i in range(args.steps):
+            step(1000 + i, use_graph=False)
+        ev1.record(stream)
+        torch.cuda.synchronize()
+        eager_ms = ev0.elapsed_time(ev1) / args.steps
+        launches, gemm_ms, flop = model.timer_read()
+        model.timer_enable(False)
+        peak = MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        achieved = flop / (gemm_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4), "traffic": None,
+                "kernel": "gemm_bf16_kernel" if m.dtype == "bf16" else "gemm_f32_kernel",
+                "launches": launches, "avg_launch_ms": round(gemm_ms / max(launches, 1), 4),
+                "gemm_share_of_step": round(gemm_ms / args.steps / eager_ms, 4)}
+        eprint(f"[bench] GEMMs: {launches} launches, {gemm_ms / args.steps:.2f} ms/step, "
+               f"{achieved:.1f} TFLOP/s; eager step {eager_ms:.2f} ms")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        eprint(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(wl, args.cpu_seconds)
+
+    value = N * R / (ms * 1e-3)
+    out = {
+        "metric": "predictor candidate-evals/sec + ms per CEM plan step (800x10) on 1 MI355X",
+        "value": round(value, 2), "unit": "candidate-evals/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": m.dtype,
+        "data": "synthetic: random-init weights N(0,0.02) (seed 0), N(0,1) embeddings (seed 1), "
+                "CEM seed 2",
+        "config": {"workload": wl.name, "n_samples": N, "n_elites": K, "rounds": R, "horizon": H,
+                   "layers": m.layers, "d_model": m.d_model, "heads": m.heads, "d_mlp": m.d_mlp,
+                   "patches": m.patches, "enc_dim": m.enc_dim, "graph_replay": True,
+                   "eager_ms_per_step": round(eager_ms, 3) if eager_ms else None},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    model.close()
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

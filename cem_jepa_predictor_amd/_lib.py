@@ -1,0 +1,198 @@
+"""ctypes binding of libcem_jepa.so: argument marshalling only.
+
+Every function here forwards torch tensors' device pointers and the current
+HIP stream to the C ABI declared in include/cem_jepa.h; all computation runs
+in the library's HIP kernels.  There is no fallback: if the library is not
+built, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import numpy as np
+
+from .inputs import ModelConfig
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libcem_jepa.so")
+
+CEM_F32, CEM_BF16 = 0, 1
+TRACE_ACTIONS, TRACE_ENERGY, TRACE_ELITES, TRACE_MU, TRACE_SIGMA = range(5)
+STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYPE",
+                -4: "CEM_E_OOM", -5: "CEM_E_HIP", -6: "CEM_E_INTERNAL"}
+
+EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
+           "cem_plan", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
+           "cem_sample", "topk_select", "cem_timer_enable", "cem_timer_read"]
+
+
+class CemError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {msg}")
+        self.status = status
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [("layers", ctypes.c_int32), ("d_model", ctypes.c_int32), ("heads", ctypes.c_int32),
+                ("d_mlp", ctypes.c_int32), ("patches", ctypes.c_int32), ("enc_dim", ctypes.c_int32),
+                ("action_dim", ctypes.c_int32), ("state_dim", ctypes.c_int32),
+                ("max_horizon", ctypes.c_int32), ("max_samples", ctypes.c_int32),
+                ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("n_samples", ctypes.c_int32), ("n_elites", ctypes.c_int32),
+                ("rounds", ctypes.c_int32), ("horizon", ctypes.c_int32),
+                ("clamp_lo", ctypes.c_float), ("clamp_hi", ctypes.c_float),
+                ("seed", ctypes.c_uint64), ("plan_id", ctypes.c_uint32),
+                ("use_graph", ctypes.c_int32)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+P = ctypes.c_void_p
+I32, U32, U64, F32, SZ = ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_float, ctypes.c_size_t
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m cem_jepa_predictor_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.cem_last_error.restype = ctypes.c_char_p
+    lib.cem_last_error.argtypes = []
+    sigs = {
+        "cem_weights_count": [ctypes.POINTER(ModelDesc), ctypes.POINTER(SZ)],
+        "cem_model_create": [ctypes.POINTER(ModelDesc), P, SZ, I32, ctypes.POINTER(P)],
+        "cem_model_destroy": [P],
+        "cem_plan": [P, ctypes.POINTER(Params), P, P, P, P, P, P, P, P],
+        "cem_plan_trace": [P, I32, P, SZ, P],
+        "predictor_rollout": [P, P, I32, I32, P, P, P, P],
+        "energy_l1": [P, I32, P, I32, I32, I32, P, P],
+        "elite_refit": [P, P, I32, I32, I32, I32, P, P, P, P],
+        "cem_sample": [P, P, I32, I32, I32, U64, U32, U32, F32, F32, P, P, P],
+        "topk_select": [P, I32, I32, P, P],
+        "cem_timer_enable": [P, I32],
+        "cem_timer_read": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
+                           ctypes.POINTER(ctypes.c_double)],
+    }
+    for name, args in sigs.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise CemError(status, load().cem_last_error().decode())
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream or None
+
+
+def model_desc(m: ModelConfig, max_samples: int, max_horizon: Optional[int] = None) -> ModelDesc:
+    return ModelDesc(m.layers, m.d_model, m.heads, m.d_mlp, m.patches, m.enc_dim, m.action_dim,
+                     m.state_dim, max_horizon or m.max_horizon, max_samples,
+                     CEM_BF16 if m.dtype == "bf16" else CEM_F32, m.ln_eps)
+
+
+def weights_count(desc: ModelDesc) -> int:
+    n = SZ(0)
+    _check(load().cem_weights_count(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+class Model:
+    """A model handle on one device (cem_model_create / cem_model_destroy)."""
+
+    def __init__(self, cfg: ModelConfig, flat_weights: np.ndarray, max_samples: int,
+                 device: int = 0, max_horizon: Optional[int] = None):
+        lib = load()
+        self.cfg = cfg
+        self.desc = model_desc(cfg, max_samples, max_horizon)
+        w = np.ascontiguousarray(flat_weights, dtype=np.float32)
+        h = P()
+        _check(lib.cem_model_create(ctypes.byref(self.desc), w.ctypes.data, w.size, device,
+                                    ctypes.byref(h)))
+        self.handle = h
+        self._last = None
+
+    def close(self) -> None:
+        if self.handle:
+            _check(load().cem_model_destroy(self.handle))
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def plan(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
+             n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,
+             clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True, stream=None):
+        p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
+                   1 if use_graph else 0)
+        _check(load().cem_plan(self.handle, ctypes.byref(p), _ptr(z_obs), _ptr(z_goal), _ptr(s0),
+                               _ptr(mu), _ptr(sigma), _ptr(action), _ptr(best_idx), _stream(stream)))
+        self._last = p
+
+    def trace(self, kind: int, out, stream=None):
+        _check(load().cem_plan_trace(self.handle, kind, _ptr(out), out.numel() * out.element_size(),
+                                     _stream(stream)))
+        return out
+
+    def rollout(self, actions, z_obs, s0, z_pred, stream=None):
+        n, h = actions.shape[0], actions.shape[1]
+        _check(load().predictor_rollout(self.handle, _ptr(actions), n, h, _ptr(z_obs), _ptr(s0),
+                                        _ptr(z_pred), _stream(stream)))
+        return z_pred
+
+    def timer_enable(self, on: bool = True):
+        _check(load().cem_timer_enable(self.handle, 1 if on else 0))
+
+    def timer_read(self):
+        n, ms, fl = ctypes.c_int64(0), ctypes.c_double(0), ctypes.c_double(0)
+        _check(load().cem_timer_read(self.handle, ctypes.byref(n), ctypes.byref(ms), ctypes.byref(fl)))
+        return n.value, ms.value, fl.value
+
+
+def energy_l1(z_pred, z_goal, energy, stream=None):
+    import torch
+
+    dt = CEM_BF16 if z_pred.dtype == torch.bfloat16 else CEM_F32
+    n, p, e = z_pred.shape
+    _check(load().energy_l1(_ptr(z_pred), dt, _ptr(z_goal), n, p, e, _ptr(energy), _stream(stream)))
+    return energy
+
+
+def elite_refit(energy, actions, k, elite_idx, mu, sigma, stream=None):
+    n, h, a = actions.shape
+    _check(load().elite_refit(_ptr(energy), _ptr(actions), n, k, h, a, _ptr(elite_idx), _ptr(mu),
+                              _ptr(sigma), _stream(stream)))
+
+
+def cem_sample(mu, sigma, n, seed, rnd, plan_id, lo, hi, actions, raw_words=None, stream=None):
+    h, a = mu.shape
+    _check(load().cem_sample(_ptr(mu), _ptr(sigma), n, h, a, seed, rnd, plan_id, lo, hi,
+                             _ptr(actions), _ptr(raw_words), _stream(stream)))
+
+
+def topk_select(energy, k, idx, stream=None):
+    _check(load().topk_select(_ptr(energy), energy.numel(), k, _ptr(idx), _stream(stream)))

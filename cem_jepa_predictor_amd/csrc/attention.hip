@@ -1,0 +1,246 @@
+// Block-causal multi-head attention of the predictor's current frame block.
+//
+// Page "Real-Time Inference for JEPA World Model Architectures with Ray",
+// section 05: the predictor is frame-causal, so at rollout step t the queries
+// of frame block t attend to the keys of blocks 0..t, and the keys/values of
+// earlier blocks come from a KV cache instead of being recomputed.  Within a
+// block attention is bidirectional.  Softmax scale 1/sqrt(dh), fp32 softmax.
+//
+// bf16 kernel (dh = 64), one 256-thread workgroup per (candidate, head):
+//  * keys/values are staged through LDS in chunks of 64 keys: K row-major
+//    (16-byte chunks XOR-swizzled by key % 8) and V transposed (Vt[dh][key],
+//    padded rows) so that both MFMA operands are contiguous LDS reads;
+//  * each wave owns query tiles of 16 rows and computes S^T = K Q^T with
+//    v_mfma_f32_16x16x32_bf16 (lane l holds 16 scores of query l % 16), then an
+//    online (running max / running sum) softmax in fp32, then
+//    O^T += V^T P^T with P taken straight from registers: the MFMA sums over
+//    its 32 key slots, and the key each slot stands for is chosen so that the
+//    lane's own scores and the matching V^T entries line up (any consistent
+//    assignment of keys to slots gives the same sum);
+//  * HBM traffic per (candidate, head) is one read of Q, K, V and one write of
+//    O: the kernel is bandwidth-bound at the V-JEPA2-AC shape.
+#include "kernels.hpp"
+
+namespace cem {
+namespace {
+
+constexpr int kDh = 64;
+constexpr int kChunk = 64;           // keys per LDS chunk
+constexpr int kVtLd = kChunk + 8;    // padded Vt row (bf16 elements)
+constexpr int kMaxTilesPerWave = 5;  // 16-row query tiles per wave -> B <= 320
+
+__device__ __forceinline__ float wave_max_q(float v) {
+  // lanes l, l^16, l^32, l^48 share query l % 16
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  v = fmaxf(v, __shfl_xor(v, 32, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum_q(float v) {
+  v += __shfl_xor(v, 16, 64);
+  v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs p) {
+  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kChunk * kDh * 2];
+  __shared__ __attribute__((aligned(16))) bf16 vt_lds[kDh * kVtLd];
+
+  const int n = blockIdx.x / p.heads, h = blockIdx.x % p.heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int B = p.B, Lk = p.nblk * B;
+  const int q_tiles = (B + 15) / 16;
+  const int g = lane >> 4, ql = lane & 15;
+  const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
+
+  const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
+
+  // per query tile: Q fragments (B operand of S^T = K Q^T), running max / sum, O^T accumulators
+  bf16x8_t qf[kMaxTilesPerWave][2];
+  float mrun[kMaxTilesPerWave], lrun[kMaxTilesPerWave];
+  f32x4_t oacc[kMaxTilesPerWave][4];
+#pragma unroll
+  for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
+    const int tile = wave + 4 * ti;
+    const int qr = min(tile * 16 + ql, B - 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qf[ti][s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+    mrun[ti] = -INFINITY;
+    lrun[ti] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const int n_chunks = (Lk + kChunk - 1) / kChunk;
+  for (int c = 0; c < n_chunks; ++c) {
+    // ---- stage 64 keys: 512 16-byte pieces of K and of V, two per thread
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int item = tid + 256 * it;
+      const int kr = item >> 3, ck = item & 7;
+      const int key = min(c * kChunk + kr, Lk - 1);
+      const int blk = key / B, row = key - blk * B;
+      const bf16* src = static_cast<const bf16*>(p.kv[blk]) + ((long long)n * B + row) * p.ldkv +
+                        h * kDh + ck * 8;
+      const uint4 kv = *reinterpret_cast<const uint4*>(src);
+      const uint4 vv = *reinterpret_cast<const uint4*>(src + p.d);
+      *reinterpret_cast<uint4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = kv;
+      const bf16* ve = reinterpret_cast<const bf16*>(&vv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vt_lds[(ck * 8 + e) * kVtLd + kr] = ve[e];
+    }
+    __syncthreads();
+
+    const int valid = Lk - c * kChunk;   // keys >= valid in this chunk are padding
+#pragma unroll
+    for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
+      const int tile = wave + 4 * ti;
+      if (tile >= q_tiles) break;
+      // S^T[key][q] for the chunk's 4 key tiles: lane holds keys 16 kt + 4 g + r, query ql
+      f32x4_t st[4];
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const int kr = kt * 16 + ql;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+              k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
+          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ti][s], st[kt], 0, 0, 0);
+        }
+      }
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = kt * 16 + 4 * g + r;
+          const float v = (key < valid) ? st[kt][r] * sl2 : -INFINITY;
+          st[kt][r] = v;
+          cmax = fmaxf(cmax, v);
+        }
+      cmax = wave_max_q(cmax);
+      const float mnew = fmaxf(mrun[ti], cmax);      // finite: every chunk has a valid key
+      const float alpha = exp2f(mrun[ti] - mnew);    // exp2(-inf) = 0 on the first chunk
+      mrun[ti] = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = exp2f(st[kt][r] - mnew);
+          st[kt][r] = e;
+          psum += e;
+        }
+      lrun[ti] = lrun[ti] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] *= alpha;
+      // O^T[dh][q] += V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
+      // 32 sg + 4 g + e (e < 4) or 32 sg + 16 + 4 g + (e - 4) (e >= 4)
+#pragma unroll
+      for (int sg = 0; sg < 2; ++sg) {
+        union { uint32_t u[4]; bf16x8_t v; } pf;
+        pf.u[0] = pack_bf16x2(st[2 * sg][0], st[2 * sg][1]);
+        pf.u[1] = pack_bf16x2(st[2 * sg][2], st[2 * sg][3]);
+        pf.u[2] = pack_bf16x2(st[2 * sg + 1][0], st[2 * sg + 1][1]);
+        pf.u[3] = pack_bf16x2(st[2 * sg + 1][2], st[2 * sg + 1][3]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          const bf16* vrow = vt_lds + (dt * 16 + ql) * kVtLd + 32 * sg + 4 * g;
+          union { uint2 u[2]; bf16x8_t v; } vf;
+          vf.u[0] = *reinterpret_cast<const uint2*>(vrow);
+          vf.u[1] = *reinterpret_cast<const uint2*>(vrow + 16);
+          oacc[ti][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[ti][dt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // lane holds O[q = 16 tile + ql][dh = 16 dt + 4 g + r]
+  bf16* obase = static_cast<bf16*>(p.o) + (long long)n * B * p.ldo + h * kDh;
+#pragma unroll
+  for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
+    const int tile = wave + 4 * ti;
+    if (tile >= q_tiles) break;
+    const float inv = 1.0f / wave_sum_q(lrun[ti]);
+    const int q = tile * 16 + ql;
+    if (q < B) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        uint2 u;
+        u.x = pack_bf16x2(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv);
+        u.y = pack_bf16x2(oacc[ti][dt][2] * inv, oacc[ti][dt][3] * inv);
+        *reinterpret_cast<uint2*>(obase + (long long)q * p.ldo + dt * 16 + 4 * g) = u;
+      }
+    }
+  }
+}
+
+// fp32: one thread per query row, keys streamed from global memory with an
+// online softmax in fp32 (expf).  Used by fp32 models (small shapes).
+template <int DH>
+__global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs p) {
+  const int n = blockIdx.x / p.heads, h = blockIdx.x % p.heads;
+  const int B = p.B;
+  for (int i = threadIdx.x; i < B; i += blockDim.x) {
+    const float* qr = static_cast<const float*>(p.q) + ((long long)n * B + i) * p.ldq + h * DH;
+    float q[DH], o[DH];
+#pragma unroll
+    for (int j = 0; j < DH; ++j) { q[j] = qr[j]; o[j] = 0.f; }
+    float m = -INFINITY, l = 0.f;
+    for (int blk = 0; blk < p.nblk; ++blk) {
+      const float* kvb = static_cast<const float*>(p.kv[blk]);
+      for (int r = 0; r < B; ++r) {
+        const float* kr = kvb + ((long long)n * B + r) * p.ldkv + h * DH;
+        const float* vr = kr + p.d;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < DH; ++j) s = fmaf(q[j], kr[j], s);
+        s *= p.scale;
+        const float mn = fmaxf(m, s);
+        const float a = expf(m - mn), e = expf(s - mn);
+        l = l * a + e;
+#pragma unroll
+        for (int j = 0; j < DH; ++j) o[j] = o[j] * a + e * vr[j];
+        m = mn;
+      }
+    }
+    float* orow = static_cast<float*>(p.o) + ((long long)n * B + i) * p.ldo + h * DH;
+    const float inv = 1.0f / l;
+#pragma unroll
+    for (int j = 0; j < DH; ++j) orow[j] = o[j] * inv;
+  }
+}
+
+}  // namespace
+
+bool attention_bf16_supports(int dh, int B) {
+  return dh == kDh && B >= 1 && B <= 16 * 4 * kMaxTilesPerWave;
+}
+bool attention_f32_supports(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
+
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  attn_bf16_kernel<<<a.n * a.heads, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream) {
+  if (a.n <= 0) return hipSuccess;
+  const int grid = a.n * a.heads;
+  switch (a.dh) {
+    case 16: attn_f32_kernel<16><<<grid, 128, 0, stream>>>(a); break;
+    case 32: attn_f32_kernel<32><<<grid, 128, 0, stream>>>(a); break;
+    case 64: attn_f32_kernel<64><<<grid, 128, 0, stream>>>(a); break;
+    case 128: attn_f32_kernel<128><<<grid, 128, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cem

@@ -1,0 +1,304 @@
+// Dense projections of the predictor: out = epilogue(A[M, K] @ Bt[N, K]^T).
+//
+// Every linear layer of the action-conditioned predictor (fused q|k|v, output
+// projection, MLP up with GELU, MLP down, frame in/out projections) goes
+// through here.  These GEMMs carry about 95% of the plan step's FLOPs at the
+// V-JEPA2-AC predictor shape (page "Real-Time Inference for JEPA World Model
+// Architectures with Ray", section 01: ~8,000 predictor evaluations per
+// action), so the bf16 kernel is MFMA-bound by design.
+//
+// bf16 kernel (gfx950):
+//  * 256 x 256 output tile per 256-thread workgroup, BK = 64; four wave64s in
+//    a 2 x 2 grid, each owning a 128 x 128 sub-tile = 4 x 4 tiles of
+//    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+//  * The MFMA's first operand is the weight tile and its second the
+//    activation tile, so each lane's accumulator quads hold 4 consecutive
+//    output columns of one output row: the epilogue reads bias / residual and
+//    writes 8-byte (bf16) vectors.
+//  * LDS double buffer (2 x 64 KB): global -> registers -> LDS, with the next
+//    K-slab's global loads in flight during the current slab's MFMAs; one
+//    barrier per slab.  Rows of 64 bf16 (128 B) are stored as eight 16-byte
+//    chunks, chunk c of row r at position c ^ (r & 7), so the 32 rows a
+//    fragment read touches spread over all banks.
+//  * Block -> tile map is XCD-aware: the dispatcher hands block b to XCD
+//    b % 8, so each XCD receives a contiguous range of logical tiles, ordered
+//    in groups of 8 row-tiles to share A and B panels in that XCD's L2.
+//  * Ragged M / N: operand loads go through buffer resources bounded at the
+//    tile's last valid row (the hardware returns zero beyond it), stores are
+//    masked.
+//  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
+//    each carries only its own epilogue code.
+//
+// Epilogue (fp32): + bias, optional exact GELU, optional residual add (the
+// output already holds the residual stream), optional column split into two
+// destinations (q -> Q buffer, k|v -> KV cache), optional output-row remap.
+#include "kernels.hpp"
+
+namespace cem {
+namespace {
+
+// ------------------------------------------------------------------ epilogue
+template <typename T> struct Store4;
+template <> struct Store4<bf16> {
+  __device__ static __forceinline__ void load(const bf16* p, float v[4]) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    v[0] = __uint_as_float(u.x << 16); v[1] = __uint_as_float(u.x & 0xffff0000u);
+    v[2] = __uint_as_float(u.y << 16); v[3] = __uint_as_float(u.y & 0xffff0000u);
+  }
+  __device__ static __forceinline__ void store(bf16* p, const float v[4]) {
+    uint2 u;
+    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(p) = u;
+  }
+};
+template <> struct Store4<float> {
+  __device__ static __forceinline__ void load(const float* p, float v[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  __device__ static __forceinline__ void store(float* p, const float v[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Four consecutive output columns n..n+3 (n % 4 == 0, N % 4 == 0) of the
+// physical output row `row`.
+enum { kEpiPlain = 0, kEpiGelu = 1, kEpiResidual = 2 };
+
+template <typename T, int KIND>
+__device__ __forceinline__ void epilogue_row4(const Epilogue& e, int N, long long row, int n,
+                                              float v[4]) {
+  if (n >= N) return;
+  if (e.bias) {
+    const float4 bb = *reinterpret_cast<const float4*>(e.bias + n);
+    v[0] += bb.x; v[1] += bb.y; v[2] += bb.z; v[3] += bb.w;
+  }
+  if constexpr (KIND == kEpiGelu) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = gelu_exact(v[i]);
+  }
+  T* p = (n < e.split) ? static_cast<T*>(e.c0) + row * e.ld0 + n
+                       : static_cast<T*>(e.c1) + row * e.ld1 + (n - e.split);
+  if constexpr (KIND == kEpiResidual) {
+    float r[4];
+    Store4<T>::load(p, r);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] += r[i];
+  }
+  Store4<T>::store(p, v);
+}
+
+// ------------------------------------------------------------------ bf16 MFMA kernel
+constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
+constexpr int TILE_BYTES = BM * BK * 2;       // 32 KB per operand slab
+constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // A slab + B slab
+constexpr int GROUP_M = 8;
+
+__device__ __forceinline__ void tile_of_block(int b, int nb, int tiles_m, int tiles_n, int& tm,
+                                              int& tn) {
+  const int xcd = b & 7, slot = b >> 3;
+  const int base = nb >> 3, rem = nb & 7;
+  const int L = xcd * base + min(xcd, rem) + slot;
+  const int per_group = GROUP_M * tiles_n;
+  const int g = L / per_group;
+  const int first_m = g * GROUP_M;
+  const int gsize = min(tiles_m - first_m, GROUP_M);
+  const int in = L - g * per_group;
+  tm = first_m + in % gsize;
+  tn = in / gsize;
+}
+
+// Buffer resource over rows [row0, row0 + rows) of a row-major bf16 matrix,
+// advanced by k elements; loads past the last valid row return zero.
+// Valid rows stay in range for every k < K <= ld: r * ld * 2 + 2k + 16 <= rows * ld * 2.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, int row0, int rows,
+                                                            int ld, int k) {
+  const uint32_t bytes = (uint32_t)rows * (uint32_t)ld * 2u - (uint32_t)k * 2u;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<bf16*>(base + (long long)row0 * ld + k), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int KIND>
+__global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
+                                                         const bf16* __restrict__ Bt, int ldb,
+                                                         int M, int N, int K, Epilogue epi) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+
+  // global -> LDS mapping: thread owns 16-byte chunk lc of rows lr + 32 i, i < 8
+  const int lc = tid & 7, lr = tid >> 3;
+  const int voff_a = lr * lda * 2 + lc * 16, step_a = 32 * lda * 2;
+  const int voff_b = lr * ldb * 2 + lc * 16, step_b = 32 * ldb * 2;
+  const int woff = lr * 128 + ((lc ^ (lr & 7)) << 4);   // + i * 32 rows * 128 B
+
+  uint4 ra_[8], rb_[8];
+  auto gload = [&](int kt) {
+    const __amdgpu_buffer_rsrc_t sa = slab_rsrc(A, m0, rows_a, lda, kt * BK);
+    const __amdgpu_buffer_rsrc_t sb = slab_rsrc(Bt, n0, rows_b, ldb, kt * BK);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      auto va = __builtin_amdgcn_raw_buffer_load_b128(sa, voff_a + i * step_a, 0, 0);
+      auto vb = __builtin_amdgcn_raw_buffer_load_b128(sb, voff_b + i * step_b, 0, 0);
+      ra_[i] = *reinterpret_cast<uint4*>(&va);
+      rb_[i] = *reinterpret_cast<uint4*>(&vb);
+    }
+  };
+  auto lstore = [&](int stage) {
+    uint8_t* sa = smem + stage * STAGE_BYTES;
+    uint8_t* sb = sa + TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      *reinterpret_cast<uint4*>(sa + woff + i * 32 * 128) = ra_[i];
+      *reinterpret_cast<uint4*>(sb + woff + i * 32 * 128) = rb_[i];
+    }
+  };
+
+  // fragment mapping: lane reads row (l % 32) of a 32-row tile, k half (l / 32)
+  const int wm = wave >> 1, wn = wave & 1;
+  const int fr = lane & 31, fk = lane >> 5;
+  const int arow = (wm * 128 + fr) * 128;
+  const int brow = (wn * 128 + fr) * 128;
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int KT = K / BK;
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) gload(kt + 1);
+    const uint8_t* sa = smem + (kt & 1) * STAGE_BYTES;
+    const uint8_t* sb = sa + TILE_BYTES;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int pc = ((2 * s + fk) ^ (fr & 7)) << 4;
+      bf16x8_t a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        a[i] = *reinterpret_cast<const bf16x8_t*>(sa + arow + i * 32 * 128 + pc);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(sb + brow + j * 32 * 128 + pc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < KT) lstore((kt + 1) & 1);
+    __syncthreads();
+  }
+
+  // D[i][j] of one MFMA: j = lane % 32 (output row), i = 8 (r / 4) + 4 (lane / 32) + r % 4
+  const int ncol = n0 + wn * 128 + 4 * fk;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + wm * 128 + i * 32 + fr;
+    if (m >= M) continue;
+    const long long row = epi.rows(m);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                      acc[i][j][4 * q + 3]};
+        epilogue_row4<bf16, KIND>(epi, N, row, ncol + j * 32 + 8 * q, v);
+      }
+  }
+}
+
+// ------------------------------------------------------------------ fp32 kernel
+// 64 x 64 tile, BK = 16, 256 threads with 4 x 4 outputs each (VALU FMA); used
+// by fp32 models, where accuracy rather than throughput is the point.
+constexpr int FBM = 64, FBN = 64, FBK = 16;
+
+template <int KIND>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(const float* __restrict__ A, int lda,
+                                                       const float* __restrict__ Bt, int ldb,
+                                                       int M, int N, int K, Epilogue epi) {
+  __shared__ float As[FBK][FBM + 4];
+  __shared__ float Bs[FBK][FBN + 4];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int m0 = blockIdx.y * FBM, n0 = blockIdx.x * FBN;
+  const int lrow = tid >> 2, lk = (tid & 3) * 4;
+  const float* pa = A + (long long)min(m0 + lrow, M - 1) * lda + lk;
+  const float* pb = Bt + (long long)min(n0 + lrow, N - 1) * ldb + lk;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += FBK) {
+    const float4 va = *reinterpret_cast<const float4*>(pa + k0);
+    const float4 vb = *reinterpret_cast<const float4*>(pb + k0);
+    As[lk + 0][lrow] = va.x; As[lk + 1][lrow] = va.y; As[lk + 2][lrow] = va.z; As[lk + 3][lrow] = va.w;
+    Bs[lk + 0][lrow] = vb.x; Bs[lk + 1][lrow] = vb.y; Bs[lk + 2][lrow] = vb.z; Bs[lk + 3][lrow] = vb.w;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < FBK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = As[kk][ty * 4 + i]; b[i] = Bs[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int m = m0 + ty * 4 + i;
+    if (m < M) epilogue_row4<float, KIND>(epi, N, epi.rows(m), n0 + tx * 4, acc[i]);
+  }
+}
+
+int epi_kind(const Epilogue& e) { return e.residual ? kEpiResidual : (e.gelu ? kEpiGelu : kEpiPlain); }
+
+}  // namespace
+
+hipError_t gemm_init() { return hipSuccess; }
+
+hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N, int K,
+                            const Epilogue& epi, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  switch (epi_kind(epi)) {
+    case kEpiGelu:
+      gemm_bf16_kernel<kEpiGelu><<<tiles, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      break;
+    case kEpiResidual:
+      gemm_bf16_kernel<kEpiResidual><<<tiles, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      break;
+    default:
+      gemm_bf16_kernel<kEpiPlain><<<tiles, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N, int K,
+                           const Epilogue& epi, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  dim3 grid((N + FBN - 1) / FBN, (M + FBM - 1) / FBM);
+  switch (epi_kind(epi)) {
+    case kEpiGelu:
+      gemm_f32_kernel<kEpiGelu><<<grid, 256, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      break;
+    case kEpiResidual:
+      gemm_f32_kernel<kEpiResidual><<<grid, 256, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      break;
+    default:
+      gemm_f32_kernel<kEpiPlain><<<grid, 256, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace cem

@@ -1,0 +1,82 @@
+// Host launchers of the gfx950 kernels.  Every launcher enqueues on `stream`
+// and returns hipGetLastError() of its launch; shape checks happen in the
+// callers (abi.cpp / model.cpp) before anything is enqueued.
+#pragma once
+
+#include "common.hpp"
+
+namespace cem {
+
+constexpr int kMaxBlocks = 8;   // frame blocks a query can attend (max horizon)
+
+// --- sampler.hip ---------------------------------------------------------
+// x[e] = clamp(mu[e % ha] + sigma[e % ha] * z[e], lo, hi), e < n * ha.
+// dev_params (nullable): uint32 {seed_lo, seed_hi, plan_id} overriding the
+// scalar arguments, so a captured graph can be re-keyed without re-capture.
+hipError_t launch_sample(const float* mu, const float* sigma, int n, int ha, uint64_t seed,
+                         uint32_t round, uint32_t plan_id, const uint32_t* dev_params, float lo,
+                         float hi, float* x, uint32_t* raw, hipStream_t stream);
+hipError_t launch_set_params(uint32_t* dev_params, uint64_t seed, uint32_t plan_id,
+                             hipStream_t stream);
+
+// --- embed.hip -------------------------------------------------------------
+template <typename T>
+hipError_t launch_convert(const float* in, T* out, long long count, hipStream_t stream);
+// Action and state token rows (rows n*B + 0 and n*B + 1 of x) for step t.
+template <typename T>
+hipError_t launch_embed_action_state(const float* X, int N, int H, int t, int A, int S,
+                                     const float* s0, const float* wa, const float* ba,
+                                     const float* ws, const float* bs, T* x, int B, int d,
+                                     hipStream_t stream);
+// Frame rows n*B + 2 + p of x = f0[p] for every candidate n.
+template <typename T>
+hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B,
+                                  hipStream_t stream);
+
+// --- layernorm.hip -----------------------------------------------------------
+// y[r] = (x[in_rows(r)] - mean) * rsqrt(var + eps) * g + b, fp32 statistics.
+template <typename T>
+hipError_t launch_layernorm(const T* x, int rows, int d, RowMap in_rows, const float* g,
+                            const float* b, float eps, T* y, hipStream_t stream);
+bool layernorm_supports(int d);
+
+// --- gemm.hip ----------------------------------------------------------------
+// out = epilogue(A[M, K] @ Bt[N, K]^T); K % 64 == 0, N % 4 == 0 (bf16: MFMA).
+hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N,
+                            int K, const Epilogue& epi, hipStream_t stream);
+hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N,
+                           int K, const Epilogue& epi, hipStream_t stream);
+hipError_t gemm_init();   // one-time function attributes (LDS size)
+
+// --- attention.hip -------------------------------------------------------------
+// Queries: rows n*B + i of q (head h at columns h*dh); keys/values of frame
+// block tau: rows n*B + j of kv[tau] (K at columns h*dh, V at d + h*dh).
+// Every key of blocks 0..nblk-1 is visible to every query (block-causal mask
+// with the queries in the last block).
+struct AttnArgs {
+  const void* q;
+  const void* kv[kMaxBlocks];
+  void* o;
+  int ldq, ldkv, ldo;
+  int n, heads, dh, d, B, nblk;
+  float scale;
+};
+hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
+bool attention_bf16_supports(int dh, int B);
+bool attention_f32_supports(int dh);
+
+// --- energy.hip ----------------------------------------------------------------
+template <typename T>
+hipError_t launch_energy(const T* zp, const float* g, int n, long long pe, float* E,
+                         hipStream_t stream);
+
+// --- select_refit.hip ---------------------------------------------------------------
+// idx[k] = k smallest (E, index) pairs; if mu != nullptr also the elites'
+// mean / population std over ha columns of X [n, ha].
+constexpr int kMaxSelect = 16384;
+hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int ha, int* idx,
+                               float* mu, float* sigma, hipStream_t stream);
+hipError_t select_init();
+
+}  // namespace cem

@@ -1,0 +1,516 @@
+// Host orchestration of the predictor rollout and the CEM plan step.
+//
+// Page "Real-Time Inference for JEPA World Model Architectures with Ray":
+//  * section 01: a planning step encodes frame and goal once, then runs ten
+//    sequential rounds of sample -> predict -> score -> keep best -> refit;
+//  * section 04: the latents stay resident for the whole plan; each round only
+//    moves candidate actions and energies;
+//  * section 05: the predictor is frame-causal (KV cache across steps).
+// Here every round runs on one GPU stream with no host synchronisation: the
+// frame projection of z_obs is computed once per plan, the round's samples,
+// energies and refit live in device buffers, and the whole R-round sequence
+// is captured once per shape as a HIP graph and replayed.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "model.hpp"
+
+namespace cem {
+
+Status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return Status::Ok();
+  Status s;
+  s.code = (e == hipErrorOutOfMemory) ? CEM_E_OOM : CEM_E_HIP;
+  s.msg = std::string(what) + ": " + hipGetErrorString(e);
+  return s;
+}
+
+#define CEM_TRY(expr, what)                               \
+  do {                                                    \
+    hipError_t _e = (expr);                               \
+    if (_e != hipSuccess) return hip_status(_e, (what));  \
+  } while (0)
+
+DeviceGuard::DeviceGuard(int device) {
+  if (hipGetDevice(&prev) != hipSuccess) prev = -1;
+  if (prev != device) (void)hipSetDevice(device);
+}
+DeviceGuard::~DeviceGuard() {
+  int cur = -1;
+  if (prev >= 0 && hipGetDevice(&cur) == hipSuccess && cur != prev) (void)hipSetDevice(prev);
+}
+
+namespace {
+
+uint16_t host_bf16(float f) {   // round to nearest even (finite inputs)
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if ((u & 0x7f800000u) == 0x7f800000u) return (uint16_t)((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
+
+// Bump layout over one allocation.
+struct Layout {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  }
+};
+
+}  // namespace
+
+size_t weights_count(const cem_model_desc& d) {
+  const size_t D = d.d_model, F = d.d_mlp, E = d.enc_dim, A = d.action_dim, S = d.state_dim;
+  const size_t per_layer = 2 * D + D * 3 * D + 3 * D + D * D + D + 2 * D + D * F + F + F * D + D;
+  return E * D + D + A * D + D + S * D + D + (size_t)d.layers * per_layer + 2 * D + D * E + E;
+}
+
+Status validate_desc(const cem_model_desc& d) {
+  auto bad = [](cem_status c, const std::string& m) { Status s; s.code = c; s.msg = m; return s; };
+  if (d.dtype != CEM_F32 && d.dtype != CEM_BF16) return bad(CEM_E_DTYPE, "dtype must be CEM_F32 or CEM_BF16");
+  if (d.layers < 1 || d.layers > 256) return bad(CEM_E_SHAPE, "layers must be in [1, 256]");
+  if (d.heads < 1 || d.d_model < 1 || d.d_model % d.heads != 0)
+    return bad(CEM_E_SHAPE, "d_model must be a positive multiple of heads");
+  if (!layernorm_supports(d.d_model))
+    return bad(CEM_E_SHAPE, "d_model must be one of 128, 256, 384, 512, 768, 1024, 1536, 2048, 4096");
+  if (d.d_mlp < 64 || d.d_mlp % 64 != 0 || d.d_mlp > 65536) return bad(CEM_E_SHAPE, "d_mlp must be a multiple of 64");
+  if (d.enc_dim < 64 || d.enc_dim % 64 != 0 || d.enc_dim > 65536) return bad(CEM_E_SHAPE, "enc_dim must be a multiple of 64");
+  if (d.patches < 1 || d.patches > 4096) return bad(CEM_E_SHAPE, "patches must be in [1, 4096]");
+  if (d.action_dim < 1 || d.action_dim > 32 || d.state_dim < 1 || d.state_dim > 32)
+    return bad(CEM_E_SHAPE, "action_dim and state_dim must be in [1, 32]");
+  if (d.max_horizon < 1 || d.max_horizon > kMaxBlocks) return bad(CEM_E_SHAPE, "max_horizon must be in [1, 8]");
+  if (d.max_horizon > 1 && d.state_dim != d.action_dim)
+    return bad(CEM_E_SHAPE, "horizon > 1 advances the state by the action: state_dim must equal action_dim");
+  if (d.max_samples < 1 || d.max_samples > kMaxSelect) return bad(CEM_E_SHAPE, "max_samples must be in [1, 16384]");
+  if (!(d.ln_eps > 0.f) || !std::isfinite(d.ln_eps)) return bad(CEM_E_ARG, "ln_eps must be positive and finite");
+  const int dh = d.d_model / d.heads, B = d.patches + 2;
+  if (d.dtype == CEM_BF16 && !attention_bf16_supports(dh, B))
+    return bad(CEM_E_SHAPE, "bf16 attention needs head dim 64 and patches + 2 <= 320");
+  if (d.dtype == CEM_F32 && !attention_f32_supports(dh))
+    return bad(CEM_E_SHAPE, "fp32 attention needs head dim 16, 32, 64 or 128");
+  const long long rows = (long long)d.max_samples * B;
+  if (rows * std::max({3LL * d.d_model, (long long)d.d_mlp, (long long)d.enc_dim}) > (1LL << 40))
+    return bad(CEM_E_SHAPE, "workspace too large");
+  if (rows > (1LL << 30)) return bad(CEM_E_SHAPE, "max_samples * (patches + 2) too large");
+  return Status::Ok();
+}
+
+Status model_create(const cem_model_desc& d, const float* host_w, int device, cem_model** out) {
+  Status v = validate_desc(d);
+  if (!v.ok()) return v;
+  int ndev = 0;
+  CEM_TRY(hipGetDeviceCount(&ndev), "hipGetDeviceCount");
+  if (device < 0 || device >= ndev) {
+    Status s; s.code = CEM_E_ARG; s.msg = "device index out of range"; return s;
+  }
+  DeviceGuard guard(device);
+  cem_model* m = new cem_model();
+  m->desc = d;
+  m->device = device;
+  m->bf16 = d.dtype == CEM_BF16;
+  m->esz = m->bf16 ? 2 : 4;
+  m->B = d.patches + 2;
+  m->rows_max = (long long)d.max_samples * m->B;
+
+  const size_t D = d.d_model, F = d.d_mlp, E = d.enc_dim, A = d.action_dim, S = d.state_dim;
+  const size_t L = d.layers, P = d.patches, es = m->esz;
+
+  // ---- weights: host staging in device layout, then one upload
+  Layout wl;
+  const size_t o_w_in = wl.take(D * E * es), o_b_in = wl.take(D * 4);
+  const size_t o_w_a = wl.take(A * D * 4), o_b_a = wl.take(D * 4);
+  const size_t o_w_s = wl.take(S * D * 4), o_b_s = wl.take(D * 4);
+  struct LO { size_t ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_1, b_1, w_2, b_2; };
+  std::vector<LO> lo(L);
+  for (size_t l = 0; l < L; ++l) {
+    lo[l].ln1_g = wl.take(D * 4); lo[l].ln1_b = wl.take(D * 4);
+    lo[l].w_qkv = wl.take(3 * D * D * es); lo[l].b_qkv = wl.take(3 * D * 4);
+    lo[l].w_o = wl.take(D * D * es); lo[l].b_o = wl.take(D * 4);
+    lo[l].ln2_g = wl.take(D * 4); lo[l].ln2_b = wl.take(D * 4);
+    lo[l].w_1 = wl.take(F * D * es); lo[l].b_1 = wl.take(F * 4);
+    lo[l].w_2 = wl.take(D * F * es); lo[l].b_2 = wl.take(D * 4);
+  }
+  const size_t o_lnf_g = wl.take(D * 4), o_lnf_b = wl.take(D * 4);
+  const size_t o_w_out = wl.take(E * D * es), o_b_out = wl.take(E * 4);
+
+  std::vector<uint8_t> hw;
+  try {
+    hw.assign(wl.off, 0);
+  } catch (const std::bad_alloc&) {
+    delete m;
+    Status s; s.code = CEM_E_OOM; s.msg = "host staging buffer"; return s;
+  }
+  const float* src = host_w;
+  auto put_vec = [&](size_t off, size_t count) {
+    std::memcpy(hw.data() + off, src, count * 4);
+    src += count;
+  };
+  // matrix stored [in, out] in the flat buffer -> [out, in] (K contiguous) in model dtype
+  auto put_mat_t = [&](size_t off, size_t in, size_t outd) {
+    for (size_t i = 0; i < in; ++i)
+      for (size_t o = 0; o < outd; ++o) {
+        const float v = src[i * outd + o];
+        const size_t dst = o * in + i;
+        if (m->bf16) {
+          const uint16_t b = host_bf16(v);
+          std::memcpy(hw.data() + off + dst * 2, &b, 2);
+        } else {
+          std::memcpy(hw.data() + off + dst * 4, &v, 4);
+        }
+      }
+    src += in * outd;
+  };
+  put_mat_t(o_w_in, E, D); put_vec(o_b_in, D);
+  put_vec(o_w_a, A * D); put_vec(o_b_a, D);
+  put_vec(o_w_s, S * D); put_vec(o_b_s, D);
+  for (size_t l = 0; l < L; ++l) {
+    put_vec(lo[l].ln1_g, D); put_vec(lo[l].ln1_b, D);
+    put_mat_t(lo[l].w_qkv, D, 3 * D); put_vec(lo[l].b_qkv, 3 * D);
+    put_mat_t(lo[l].w_o, D, D); put_vec(lo[l].b_o, D);
+    put_vec(lo[l].ln2_g, D); put_vec(lo[l].ln2_b, D);
+    put_mat_t(lo[l].w_1, D, F); put_vec(lo[l].b_1, F);
+    put_mat_t(lo[l].w_2, F, D); put_vec(lo[l].b_2, D);
+  }
+  put_vec(o_lnf_g, D); put_vec(o_lnf_b, D);
+  put_mat_t(o_w_out, D, E); put_vec(o_b_out, E);
+
+  auto fail = [&](Status s) { model_destroy(m); return s; };
+  hipError_t e = hipMalloc(&m->warena, wl.off);
+  if (e != hipSuccess) return fail(hip_status(e, "hipMalloc(weights)"));
+  e = hipMemcpy(m->warena, hw.data(), wl.off, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(hip_status(e, "hipMemcpy(weights)"));
+  uint8_t* wb = static_cast<uint8_t*>(m->warena);
+  m->w_in_t = wb + o_w_in; m->b_in = (float*)(wb + o_b_in);
+  m->w_a = (float*)(wb + o_w_a); m->b_a = (float*)(wb + o_b_a);
+  m->w_s = (float*)(wb + o_w_s); m->b_s = (float*)(wb + o_b_s);
+  m->layers.resize(L);
+  for (size_t l = 0; l < L; ++l) {
+    LayerW& w = m->layers[l];
+    w.ln1_g = (float*)(wb + lo[l].ln1_g); w.ln1_b = (float*)(wb + lo[l].ln1_b);
+    w.w_qkv_t = wb + lo[l].w_qkv; w.b_qkv = (float*)(wb + lo[l].b_qkv);
+    w.w_o_t = wb + lo[l].w_o; w.b_o = (float*)(wb + lo[l].b_o);
+    w.ln2_g = (float*)(wb + lo[l].ln2_g); w.ln2_b = (float*)(wb + lo[l].ln2_b);
+    w.w_1_t = wb + lo[l].w_1; w.b_1 = (float*)(wb + lo[l].b_1);
+    w.w_2_t = wb + lo[l].w_2; w.b_2 = (float*)(wb + lo[l].b_2);
+  }
+  m->lnf_g = (float*)(wb + o_lnf_g); m->lnf_b = (float*)(wb + o_lnf_b);
+  m->w_out_t = wb + o_w_out; m->b_out = (float*)(wb + o_b_out);
+
+  // ---- workspace
+  const size_t rows = (size_t)m->rows_max;
+  const size_t kv_slots = L * (size_t)(d.max_horizon - 1) + 1;
+  Layout al;
+  const size_t o_x = al.take(rows * D * es), o_h = al.take(rows * D * es), o_q = al.take(rows * D * es);
+  const size_t o_u = al.take(rows * F * es);
+  const size_t o_kv = al.take(kv_slots * rows * 2 * D * es);
+  const size_t o_zhat = al.take((size_t)d.max_samples * P * E * es);
+  const size_t o_f0 = al.take(P * D * es), o_zobs = al.take(P * E * es);
+  e = hipMalloc(&m->arena, al.off);
+  if (e != hipSuccess) return fail(hip_status(e, "hipMalloc(workspace)"));
+  uint8_t* ab = static_cast<uint8_t*>(m->arena);
+  m->x = ab + o_x; m->h = ab + o_h; m->q = ab + o_q; m->u = ab + o_u; m->kv = ab + o_kv;
+  m->zhat = ab + o_zhat; m->f0 = ab + o_f0; m->zobs_t = ab + o_zobs;
+
+  e = select_init();
+  if (e != hipSuccess) return fail(hip_status(e, "select_init"));
+  e = gemm_init();
+  if (e != hipSuccess) return fail(hip_status(e, "gemm_init"));
+  e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
+  if (e != hipSuccess) return fail(hip_status(e, "hipStreamCreate"));
+  *out = m;
+  return Status::Ok();
+}
+
+void model_destroy(cem_model* m) {
+  if (!m) return;
+  DeviceGuard guard(m->device);
+  (void)hipDeviceSynchronize();
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  for (auto& pr : m->ev) { (void)hipEventDestroy(pr.first); (void)hipEventDestroy(pr.second); }
+  if (m->plan.mem) (void)hipFree(m->plan.mem);
+  if (m->arena) (void)hipFree(m->arena);
+  if (m->warena) (void)hipFree(m->warena);
+  if (m->cap_stream) (void)hipStreamDestroy(m->cap_stream);
+  delete m;
+}
+
+namespace {
+
+// ---------------------------------------------------------------- timers
+hipError_t timer_start(cem_model* m, hipStream_t st, double flop) {
+  if (!m->timers) return hipSuccess;
+  if (m->ev_used == m->ev.size()) {
+    std::pair<hipEvent_t, hipEvent_t> pr;
+    hipError_t e = hipEventCreate(&pr.first);
+    if (e != hipSuccess) return e;
+    e = hipEventCreate(&pr.second);
+    if (e != hipSuccess) return e;
+    m->ev.push_back(pr);
+    m->ev_flop.push_back(0.0);
+  }
+  m->ev_flop[m->ev_used] = flop;
+  return hipEventRecord(m->ev[m->ev_used].first, st);
+}
+hipError_t timer_stop(cem_model* m, hipStream_t st) {
+  if (!m->timers) return hipSuccess;
+  return hipEventRecord(m->ev[m->ev_used++].second, st);
+}
+
+hipError_t gemm(cem_model* m, const void* A, int lda, const void* Bt, int ldb, int M, int N, int K,
+                const Epilogue& e, hipStream_t st) {
+  hipError_t r = timer_start(m, st, 2.0 * M * (double)N * K);
+  if (r != hipSuccess) return r;
+  r = m->bf16 ? launch_gemm_bf16(static_cast<const bf16*>(A), lda, static_cast<const bf16*>(Bt),
+                                 ldb, M, N, K, e, st)
+              : launch_gemm_f32(static_cast<const float*>(A), lda,
+                                static_cast<const float*>(Bt), ldb, M, N, K, e, st);
+  if (r != hipSuccess) return r;
+  return timer_stop(m, st);
+}
+
+Epilogue epi(const float* bias, void* c0, int ld0, int split, void* c1 = nullptr, int ld1 = 0,
+             int gelu = 0, int residual = 0, RowMap rows = RowMap::identity()) {
+  Epilogue e;
+  e.bias = bias; e.c0 = c0; e.c1 = c1; e.ld0 = ld0; e.ld1 = ld1; e.split = split;
+  e.gelu = gelu; e.residual = residual; e.rows = rows;
+  return e;
+}
+
+void* kv_slot(cem_model* m, int l, int tau, int horizon) {
+  const size_t slot = (tau < horizon - 1) ? (size_t)l * (m->desc.max_horizon - 1) + tau
+                                          : (size_t)m->desc.layers * (m->desc.max_horizon - 1);
+  return static_cast<uint8_t*>(m->kv) + slot * (size_t)m->rows_max * 2 * m->desc.d_model * m->esz;
+}
+
+// f0 = z_obs W_in + b_in, shared by every candidate's first frame block.
+template <typename T>
+hipError_t enqueue_frame0(cem_model* m, const float* z_obs, hipStream_t st) {
+  const int P = m->desc.patches, E = m->desc.enc_dim, D = m->desc.d_model;
+  // stage z_obs (caller memory, 4-byte aligned) into the aligned model-dtype buffer
+  hipError_t r = launch_convert<T>(z_obs, static_cast<T*>(m->zobs_t), (long long)P * E, st);
+  if (r != hipSuccess) return r;
+  return gemm(m, m->zobs_t, E, m->w_in_t, E, P, D, E, epi(m->b_in, m->f0, D, D), st);
+}
+
+// Autoregressive block-causal rollout of n candidates; leaves z_H in m->zhat.
+template <typename T>
+hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const float* s0,
+                           hipStream_t st) {
+  const cem_model_desc& d = m->desc;
+  const int B = m->B, P = d.patches, D = d.d_model, F = d.d_mlp, E = d.enc_dim;
+  const int rows = n * B;
+  hipError_t r;
+#define RUN(x) do { r = (x); if (r != hipSuccess) return r; } while (0)
+  for (int t = 0; t < H; ++t) {
+    RUN(launch_embed_action_state<T>(X, n, H, t, d.action_dim, d.state_dim, s0, m->w_a, m->b_a,
+                                     m->w_s, m->b_s, static_cast<T*>(m->x), B, D, st));
+    if (t == 0) {
+      RUN(launch_broadcast_frame<T>(static_cast<const T*>(m->f0), P, D, static_cast<T*>(m->x), n, B, st));
+    } else {
+      // frame rows of block t = previous prediction projected in (row r -> n B + 2 + p)
+      RUN(gemm(m, m->zhat, E, m->w_in_t, E, n * P, D, E,
+               epi(m->b_in, m->x, D, D, nullptr, 0, 0, 0, RowMap{P, B, 2}), st));
+    }
+    for (int l = 0; l < d.layers; ++l) {
+      const LayerW& w = m->layers[l];
+      RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
+                              w.ln1_b, d.ln_eps, static_cast<T*>(m->h), st));
+      RUN(gemm(m, m->h, D, w.w_qkv_t, D, rows, 3 * D, D,
+               epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
+      AttnArgs a{};
+      a.q = m->q; a.ldq = D;
+      for (int tau = 0; tau <= t; ++tau) a.kv[tau] = kv_slot(m, l, tau, H);
+      a.ldkv = 2 * D; a.o = m->h; a.ldo = D;
+      a.n = n; a.heads = d.heads; a.dh = D / d.heads; a.d = D; a.B = B; a.nblk = t + 1;
+      a.scale = 1.0f / std::sqrt((float)a.dh);
+      RUN(m->bf16 ? launch_attention_bf16(a, st) : launch_attention_f32(a, st));
+      RUN(gemm(m, m->h, D, w.w_o_t, D, rows, D, D, epi(w.b_o, m->x, D, D, nullptr, 0, 0, 1), st));
+      RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
+                              w.ln2_b, d.ln_eps, static_cast<T*>(m->h), st));
+      RUN(gemm(m, m->h, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
+      RUN(gemm(m, m->u, F, w.w_2_t, F, rows, D, F, epi(w.b_2, m->x, D, D, nullptr, 0, 0, 1), st));
+    }
+    // final LayerNorm of the patch rows, then the out-projection to the encoder width
+    RUN(launch_layernorm<T>(static_cast<const T*>(m->x), n * P, D, RowMap{P, B, 2}, m->lnf_g,
+                            m->lnf_b, d.ln_eps, static_cast<T*>(m->h), st));
+    RUN(gemm(m, m->h, D, m->w_out_t, D, n * P, E, D, epi(m->b_out, m->zhat, E, E), st));
+  }
+#undef RUN
+  return hipSuccess;
+}
+
+template <typename T>
+hipError_t enqueue_plan_body(cem_model* m, const cem_params& p, hipStream_t st) {
+  PlanState& ps = m->plan;
+  const int N = p.n_samples, K = p.n_elites, H = p.horizon, ha = H * m->desc.action_dim;
+  const long long pe = (long long)m->desc.patches * m->desc.enc_dim;
+  hipError_t r = enqueue_frame0<T>(m, ps.zobs, st);
+  if (r != hipSuccess) return r;
+  for (int rd = 0; rd < p.rounds; ++rd) {
+    float* x = ps.x_hist + (size_t)rd * N * ha;
+    r = launch_sample(ps.mu_hist + (size_t)rd * ha, ps.sigma_hist + (size_t)rd * ha, N, ha, p.seed,
+                      (uint32_t)rd, p.plan_id, ps.params, p.clamp_lo, p.clamp_hi, x, nullptr, st);
+    if (r != hipSuccess) return r;
+    r = enqueue_rollout<T>(m, x, N, H, ps.s0, st);
+    if (r != hipSuccess) return r;
+    r = launch_energy<T>(static_cast<const T*>(m->zhat), ps.zgoal, N, pe, ps.e_hist + (size_t)rd * N, st);
+    if (r != hipSuccess) return r;
+    r = launch_select_refit(ps.e_hist + (size_t)rd * N, x, N, K, ha, ps.elites + (size_t)rd * K,
+                            ps.mu_hist + (size_t)(rd + 1) * ha, ps.sigma_hist + (size_t)(rd + 1) * ha, st);
+    if (r != hipSuccess) return r;
+  }
+  return hipSuccess;
+}
+
+Status ensure_plan_state(cem_model* m, const cem_params& p) {
+  PlanState& ps = m->plan;
+  const int ha = p.horizon * m->desc.action_dim;
+  if (ps.mem && p.n_samples <= ps.n && p.n_elites <= ps.k && p.rounds <= ps.r && ha <= ps.ha)
+    return Status::Ok();
+  const int n = std::max(p.n_samples, ps.n), k = std::max(p.n_elites, ps.k);
+  const int r = std::max(p.rounds, ps.r), hh = std::max(ha, ps.ha);
+  const size_t PE = (size_t)m->desc.patches * m->desc.enc_dim;
+  Layout l;
+  const size_t o_x = l.take((size_t)r * n * hh * 4), o_e = l.take((size_t)r * n * 4);
+  const size_t o_mu = l.take((size_t)(r + 1) * hh * 4), o_sg = l.take((size_t)(r + 1) * hh * 4);
+  const size_t o_el = l.take((size_t)r * k * 4);
+  const size_t o_zo = l.take(PE * 4), o_zg = l.take(PE * 4), o_s0 = l.take(64 * 4), o_pp = l.take(16);
+  // existing graphs reference the old buffers
+  CEM_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
+  for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
+  m->graphs.clear();
+  if (ps.mem) { (void)hipFree(ps.mem); ps.mem = nullptr; }
+  CEM_TRY(hipMalloc(&ps.mem, l.off), "hipMalloc(plan state)");
+  uint8_t* b = static_cast<uint8_t*>(ps.mem);
+  ps.n = n; ps.k = k; ps.r = r; ps.ha = hh;
+  ps.x_hist = (float*)(b + o_x); ps.e_hist = (float*)(b + o_e);
+  ps.mu_hist = (float*)(b + o_mu); ps.sigma_hist = (float*)(b + o_sg);
+  ps.elites = (int*)(b + o_el);
+  ps.zobs = (float*)(b + o_zo); ps.zgoal = (float*)(b + o_zg); ps.s0 = (float*)(b + o_s0);
+  ps.params = (uint32_t*)(b + o_pp);
+  return Status::Ok();
+}
+
+template <typename T>
+Status run_plan(cem_model* m, const cem_params& p, hipStream_t st) {
+  if (!p.use_graph || m->timers) return hip_status(enqueue_plan_body<T>(m, p, st), "plan kernels");
+  uint32_t lo_bits, hi_bits;
+  std::memcpy(&lo_bits, &p.clamp_lo, 4);
+  std::memcpy(&hi_bits, &p.clamp_hi, 4);
+  const GraphKey key{p.n_samples, p.n_elites, p.rounds, p.horizon, lo_bits, hi_bits};
+  auto it = m->graphs.find(key);
+  if (it == m->graphs.end()) {
+    CEM_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
+    const hipError_t body = enqueue_plan_body<T>(m, p, m->cap_stream);
+    hipGraph_t g = nullptr;
+    const hipError_t end = hipStreamEndCapture(m->cap_stream, &g);
+    if (body != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_status(body, "plan capture"); }
+    CEM_TRY(end, "hipStreamEndCapture");
+    hipGraphExec_t exec = nullptr;
+    const hipError_t inst = hipGraphInstantiate(&exec, g, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g);
+    CEM_TRY(inst, "hipGraphInstantiate");
+    it = m->graphs.emplace(key, exec).first;
+  }
+  CEM_TRY(hipGraphLaunch(it->second, st), "hipGraphLaunch");
+  return Status::Ok();
+}
+
+}  // namespace
+
+Status rollout(cem_model* m, const float* actions, int n, int horizon, const float* z_obs,
+               const float* s0, void* z_pred, hipStream_t st) {
+  DeviceGuard guard(m->device);
+  hipError_t r = m->bf16 ? enqueue_frame0<bf16>(m, z_obs, st) : enqueue_frame0<float>(m, z_obs, st);
+  if (r != hipSuccess) return hip_status(r, "frame projection");
+  r = m->bf16 ? enqueue_rollout<bf16>(m, actions, n, horizon, s0, st)
+              : enqueue_rollout<float>(m, actions, n, horizon, s0, st);
+  if (r != hipSuccess) return hip_status(r, "rollout kernels");
+  const size_t bytes = (size_t)n * m->desc.patches * m->desc.enc_dim * m->esz;
+  CEM_TRY(hipMemcpyAsync(z_pred, m->zhat, bytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync(z_pred)");
+  return Status::Ok();
+}
+
+Status plan(cem_model* m, const cem_params& p, const float* z_obs, const float* z_goal,
+            const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
+            hipStream_t st) {
+  DeviceGuard guard(m->device);
+  Status s = ensure_plan_state(m, p);
+  if (!s.ok()) return s;
+  PlanState& ps = m->plan;
+  const size_t PE = (size_t)m->desc.patches * m->desc.enc_dim;
+  const int A = m->desc.action_dim, ha = p.horizon * A;
+  CEM_TRY(hipMemcpyAsync(ps.zobs, z_obs, PE * 4, hipMemcpyDeviceToDevice, st), "copy z_obs");
+  CEM_TRY(hipMemcpyAsync(ps.zgoal, z_goal, PE * 4, hipMemcpyDeviceToDevice, st), "copy z_goal");
+  CEM_TRY(hipMemcpyAsync(ps.s0, s0, (size_t)m->desc.state_dim * 4, hipMemcpyDeviceToDevice, st), "copy s0");
+  CEM_TRY(hipMemcpyAsync(ps.mu_hist, mu, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy mu");
+  CEM_TRY(hipMemcpyAsync(ps.sigma_hist, sigma, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma");
+  CEM_TRY(launch_set_params(ps.params, p.seed, p.plan_id, st), "set params");
+  s = m->bf16 ? run_plan<bf16>(m, p, st) : run_plan<float>(m, p, st);
+  if (!s.ok()) return s;
+  const float* mu_r = ps.mu_hist + (size_t)p.rounds * ha;
+  const float* sg_r = ps.sigma_hist + (size_t)p.rounds * ha;
+  CEM_TRY(hipMemcpyAsync(mu, mu_r, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy mu out");
+  CEM_TRY(hipMemcpyAsync(sigma, sg_r, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma out");
+  CEM_TRY(hipMemcpyAsync(action, mu_r, (size_t)A * 4, hipMemcpyDeviceToDevice, st), "copy action");
+  if (best_idx)
+    CEM_TRY(hipMemcpyAsync(best_idx, ps.elites + (size_t)(p.rounds - 1) * p.n_elites, 4,
+                           hipMemcpyDeviceToDevice, st), "copy best_idx");
+  ps.last_n = p.n_samples; ps.last_k = p.n_elites; ps.last_r = p.rounds; ps.last_h = p.horizon;
+  return Status::Ok();
+}
+
+Status plan_trace(cem_model* m, int kind, void* dst, size_t bytes, hipStream_t st) {
+  DeviceGuard guard(m->device);
+  const PlanState& ps = m->plan;
+  Status bad;
+  bad.code = CEM_E_ARG;
+  if (!ps.mem || ps.last_r == 0) { bad.msg = "no plan has run on this model"; return bad; }
+  const size_t N = ps.last_n, K = ps.last_k, R = ps.last_r, ha = (size_t)ps.last_h * m->desc.action_dim;
+  const void* src = nullptr;
+  size_t want = 0;
+  switch (kind) {
+    case CEM_TRACE_ACTIONS: src = ps.x_hist; want = R * N * ha * 4; break;
+    case CEM_TRACE_ENERGY: src = ps.e_hist; want = R * N * 4; break;
+    case CEM_TRACE_ELITES: src = ps.elites; want = R * K * 4; break;
+    case CEM_TRACE_MU: src = ps.mu_hist; want = (R + 1) * ha * 4; break;
+    case CEM_TRACE_SIGMA: src = ps.sigma_hist; want = (R + 1) * ha * 4; break;
+    default: bad.msg = "unknown trace kind"; return bad;
+  }
+  if (bytes != want) {
+    bad.code = CEM_E_SHAPE;
+    bad.msg = "trace size mismatch: expected " + std::to_string(want) + " bytes";
+    return bad;
+  }
+  CEM_TRY(hipMemcpyAsync(dst, src, bytes, hipMemcpyDeviceToDevice, st), "copy trace");
+  return Status::Ok();
+}
+
+Status timer_read(cem_model* m, int64_t* launches, double* ms, double* flop) {
+  DeviceGuard guard(m->device);
+  double tot = 0.0, fl = 0.0;
+  for (size_t i = 0; i < m->ev_used; ++i) {
+    CEM_TRY(hipEventSynchronize(m->ev[i].second), "hipEventSynchronize");
+    float t = 0.f;
+    CEM_TRY(hipEventElapsedTime(&t, m->ev[i].first, m->ev[i].second), "hipEventElapsedTime");
+    tot += t;
+    fl += m->ev_flop[i];
+  }
+  *launches = (int64_t)m->ev_used;
+  *ms = tot;
+  *flop = fl;
+  m->ev_used = 0;
+  return Status::Ok();
+}
+
+}  // namespace cem

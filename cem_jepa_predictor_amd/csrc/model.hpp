@@ -1,0 +1,101 @@
+// Host-side model: device weights, workspace, and the enqueue sequences of
+// the predictor rollout and of the CEM plan step.
+#pragma once
+
+#include <map>
+#include <string>
+#include <tuple>
+#include <utility>
+#include <vector>
+
+#include "cem_jepa.h"
+#include "kernels.hpp"
+
+namespace cem {
+
+struct Status {
+  cem_status code = CEM_OK;
+  std::string msg;
+  bool ok() const { return code == CEM_OK; }
+  static Status Ok() { return {}; }
+};
+Status hip_status(hipError_t e, const char* what);
+
+// RAII: make `device` current, restore the previous device on exit.
+struct DeviceGuard {
+  int prev = -1;
+  explicit DeviceGuard(int device);
+  ~DeviceGuard();
+};
+
+struct LayerW {
+  float *ln1_g, *ln1_b, *b_qkv, *b_o, *ln2_g, *ln2_b, *b_1, *b_2;
+  void *w_qkv_t, *w_o_t, *w_1_t, *w_2_t;   // transposed: [out, in]
+};
+
+// Per-plan-shape device state: inputs copied in, per-round history out.
+struct PlanState {
+  int n = 0, k = 0, r = 0, h = 0, ha = 0;
+  void* mem = nullptr;
+  float *x_hist = nullptr, *e_hist = nullptr, *mu_hist = nullptr, *sigma_hist = nullptr;
+  int* elites = nullptr;
+  float *zobs = nullptr, *zgoal = nullptr, *s0 = nullptr;
+  uint32_t* params = nullptr;
+  int last_n = 0, last_k = 0, last_r = 0, last_h = 0;   // shape of the last plan run
+};
+
+using GraphKey = std::tuple<int, int, int, int, uint32_t, uint32_t>;
+
+}  // namespace cem
+
+struct cem_model {
+  cem_model_desc desc{};
+  int device = 0;
+  bool bf16 = false;
+  size_t esz = 4;        // bytes per weight / activation element
+  int B = 0;             // tokens per frame block
+  long long rows_max = 0;
+
+  void* warena = nullptr;
+  void* arena = nullptr;
+
+  // weights
+  void* w_in_t = nullptr;  // [d, E]
+  float* b_in = nullptr;
+  float *w_a = nullptr, *b_a = nullptr, *w_s = nullptr, *b_s = nullptr;  // fp32 [A|S, d], [d]
+  std::vector<cem::LayerW> layers;
+  float *lnf_g = nullptr, *lnf_b = nullptr, *b_out = nullptr;
+  void* w_out_t = nullptr;  // [E, d]
+
+  // workspace
+  void *x = nullptr, *h = nullptr, *q = nullptr, *u = nullptr, *kv = nullptr, *zhat = nullptr,
+       *f0 = nullptr, *zobs_t = nullptr;
+
+  cem::PlanState plan;
+  hipStream_t cap_stream = nullptr;
+  std::map<cem::GraphKey, hipGraphExec_t> graphs;
+
+  // kernel timers (dense GEMMs)
+  bool timers = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+  std::vector<double> ev_flop;
+  size_t ev_used = 0;
+};
+
+namespace cem {
+
+Status model_create(const cem_model_desc& d, const float* host_w, int device, cem_model** out);
+void model_destroy(cem_model* m);
+
+Status rollout(cem_model* m, const float* actions, int n, int horizon, const float* z_obs,
+               const float* s0, void* z_pred, hipStream_t st);
+Status plan(cem_model* m, const cem_params& p, const float* z_obs, const float* z_goal,
+            const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
+            hipStream_t st);
+Status plan_trace(cem_model* m, int kind, void* dst, size_t bytes, hipStream_t st);
+Status timer_read(cem_model* m, int64_t* launches, double* ms, double* flop);
+
+size_t weights_count(const cem_model_desc& d);
+Status validate_desc(const cem_model_desc& d);
+
+}  // namespace cem

@@ -1,0 +1,83 @@
+// Top-K elite selection and Gaussian refit.
+//
+// Page "Real-Time Inference for JEPA World Model Architectures with Ray",
+// section 01: after scoring, the search keeps the best 80 of the 800
+// candidates and re-centres the Gaussian on them.  Selection key: the 64-bit
+// word (orderable(energy) << 32) | index, so equal energies rank by index and
+// the elite list is unique; NaN ranks as +inf and -0 as +0.  Refit: mean and
+// population std of the elites' clamped samples per (step, action dim),
+// accumulated in float64 in elite order, rounded to float32.
+//
+// One 1024-thread workgroup: a bitonic sort of the padded key array in LDS
+// (n <= 16384 keys = 128 KB), then the first k keys give the elites.  The
+// whole step is a few microseconds: it is launch-latency bound.
+#include "kernels.hpp"
+
+namespace cem {
+namespace {
+
+__device__ __forceinline__ uint64_t select_key(float e, int i) {
+  uint32_t u = __float_as_uint(e);
+  if (e != e) u = 0x7f800000u;          // NaN ranks as +inf
+  if (u == 0x80000000u) u = 0u;          // -0 ranks as +0
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)ord << 32) | (uint32_t)i;
+}
+
+__global__ __launch_bounds__(1024) void select_refit_kernel(const float* __restrict__ E,
+                                                            const float* __restrict__ X, int n,
+                                                            int npad, int k, int ha,
+                                                            int* __restrict__ idx,
+                                                            float* __restrict__ mu,
+                                                            float* __restrict__ sigma) {
+  extern __shared__ uint64_t keys[];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < npad; i += blockDim.x) keys[i] = i < n ? select_key(E[i], i) : ~0ull;
+  __syncthreads();
+  for (int size = 2; size <= npad; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int i = tid; i < (npad >> 1); i += blockDim.x) {
+        const int lo = (i / stride) * 2 * stride + (i % stride), hi = lo + stride;
+        const bool ascending = (lo & size) == 0;
+        const uint64_t a = keys[lo], b = keys[hi];
+        if ((a > b) == ascending) { keys[lo] = b; keys[hi] = a; }
+      }
+      __syncthreads();
+    }
+  }
+  for (int i = tid; i < k; i += blockDim.x) idx[i] = (int)(uint32_t)keys[i];
+  if (mu) {
+    for (int j = tid; j < ha; j += blockDim.x) {
+      double s = 0.0;
+      for (int i = 0; i < k; ++i) s += (double)X[(long long)(uint32_t)keys[i] * ha + j];
+      const double mean = s / (double)k;
+      double v = 0.0;
+      for (int i = 0; i < k; ++i) {
+        const double dlt = (double)X[(long long)(uint32_t)keys[i] * ha + j] - mean;
+        v += dlt * dlt;
+      }
+      mu[j] = (float)mean;
+      sigma[j] = (float)sqrt(v / (double)k);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t select_init() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&select_refit_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             kMaxSelect * (int)sizeof(uint64_t));
+}
+
+hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int ha, int* idx,
+                               float* mu, float* sigma, hipStream_t stream) {
+  if (n <= 0 || k <= 0) return hipSuccess;
+  int npad = 2;
+  while (npad < n) npad <<= 1;
+  select_refit_kernel<<<1, 1024, npad * sizeof(uint64_t), stream>>>(E, X, n, npad, k, ha, idx, mu,
+                                                                      sigma);
+  return hipGetLastError();
+}
+
+}  // namespace cem

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports what include/cem_jepa.h declares, and
+rejects bad arguments on the host before any device work (no GPU needed)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from cem_jepa_predictor_amd import _lib, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cem_jepa.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libcem_jepa.so is not built (python -m cem_jepa_predictor_amd.build)")
+    return _lib.load()
+
+
+def test_header_declares_the_boundary():
+    fns = declared_functions()
+    for name in ["cem_plan", "predictor_rollout", "energy_l1", "elite_refit", "cem_model_create",
+                 "cem_model_destroy", "cem_last_error", "cem_sample", "topk_select"]:
+        assert name in fns
+    assert set(fns) == set(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_weights_count_matches_canonical_layout(lib):
+    for name in ["tiny", "small", "vjepa2ac", "vjepa2ac_h4"]:
+        m = inputs.WORKLOADS[name].model
+        desc = _lib.model_desc(m, 8)
+        assert _lib.weights_count(desc) == inputs.weight_count(m)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("d_model", 100, -2), ("heads", 3, -2), ("d_mlp", 100, -2), ("enc_dim", 30, -2),
+    ("max_horizon", 9, -2), ("max_samples", 0, -2), ("max_samples", 20000, -2), ("dtype", 7, -3),
+    ("layers", 0, -2), ("patches", 0, -2), ("ln_eps", 0.0, -1), ("action_dim", 0, -2),
+])
+def test_model_desc_validation(lib, field, value, status):
+    m = inputs.WORKLOADS["tiny"].model
+    desc = _lib.model_desc(m, 8)
+    setattr(desc, field, value)
+    n = ctypes.c_size_t(0)
+    assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == status
+    assert lib.cem_last_error().decode() != ""
+
+
+def test_bf16_attention_shape_limits(lib):
+    m = inputs.WORKLOADS["small"].model
+    desc = _lib.model_desc(m, 8)
+    desc.heads = 4   # head dim 128: the bf16 attention kernel takes 64
+    n = ctypes.c_size_t(0)
+    assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == -2
+    desc = _lib.model_desc(m, 8)
+    desc.patches = 400   # 402 tokens per block exceeds the per-wave query tiles
+    assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == -2
+
+
+def test_create_rejects_wrong_weight_count_and_nonfinite(lib):
+    m = inputs.WORKLOADS["tiny"].model
+    desc = _lib.model_desc(m, 8)
+    w = np.zeros(inputs.weight_count(m) - 1, np.float32)
+    h = ctypes.c_void_p()
+    assert lib.cem_model_create(ctypes.byref(desc), w.ctypes.data, w.size, 0, ctypes.byref(h)) == -2
+    w = np.zeros(inputs.weight_count(m), np.float32)
+    w[5] = np.nan
+    assert lib.cem_model_create(ctypes.byref(desc), w.ctypes.data, w.size, 0, ctypes.byref(h)) == -1
+    assert "non-finite" in lib.cem_last_error().decode()
+    assert lib.cem_model_create(None, w.ctypes.data, w.size, 0, ctypes.byref(h)) == -1
+
+
+def test_model_free_calls_validate_before_launch(lib):
+    fake = ctypes.c_void_p(0x1000)   # never dereferenced: validation fails first
+    assert lib.energy_l1(None, 0, fake, 1, 1, 1, fake, None) == -1
+    assert lib.energy_l1(fake, 5, fake, 1, 1, 1, fake, None) == -3
+    assert lib.energy_l1(fake, 0, fake, -1, 1, 1, fake, None) == -2
+    assert lib.elite_refit(fake, fake, 10, 11, 1, 7, fake, fake, fake, None) == -2
+    assert lib.elite_refit(fake, fake, 20000, 10, 1, 7, fake, fake, fake, None) == -2
+    assert lib.elite_refit(fake, fake, 10, 0, 1, 7, fake, fake, fake, None) == -2
+    assert lib.topk_select(fake, 0, 1, fake, None) == -2
+    assert lib.cem_sample(fake, fake, 4, 1, 7, 0, 0, 0, 1.0, -1.0, fake, None, None) == -1
+    assert lib.cem_sample(fake, fake, 4, 1, 7, 0, 0, 0, float("nan"), 1.0, fake, None, None) == -1
+    assert lib.energy_l1(ctypes.c_void_p(0x1001), 0, fake, 1, 1, 1, fake, None) == -1   # misaligned
+
+
+def test_plan_calls_validate_null_model(lib):
+    p = _lib.Params(8, 2, 1, 1, -1.0, 1.0, 0, 0, 1)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.cem_plan(None, ctypes.byref(p), fake, fake, fake, fake, fake, fake, None, None) == -1
+    assert lib.predictor_rollout(None, fake, 1, 1, fake, fake, fake, None) == -1
+    assert lib.cem_plan_trace(None, 0, fake, 4, None) == -1
+    assert lib.cem_timer_enable(None, 1) == -1

@@ -1,0 +1,127 @@
+"""GPU parity of the search kernels against the oracle (sampler, top-K, refit, energy)."""
+import numpy as np
+import pytest
+
+from oracle import energy as o_energy
+from oracle import refit as o_refit
+from oracle import sampler as o_sampler
+from oracle import select as o_select
+
+from .gpu_util import log, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("n,h,seed,rnd,plan", [(800, 1, 2, 0, 0), (3, 1, 5, 7, 1), (3200, 4, 2, 9, 3),
+                                                 (1, 2, 2**64 - 1, 2**32 - 1, 2**32 - 1), (0, 1, 1, 1, 1)])
+def test_sampler_matches_oracle(gpu_lib, n, h, seed, rnd, plan):
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    log(f"sampler n={n} h={h} seed={seed} round={rnd} plan={plan}")
+    a = 7
+    rng = np.random.default_rng(n + h)
+    mu = rng.uniform(-0.5, 0.5, (h, a)).astype(np.float32)
+    sigma = rng.uniform(0.0, 1.2, (h, a)).astype(np.float32)
+    x = torch.empty((max(n, 1), h, a), dtype=torch.float32, device="cuda")
+    raw = torch.empty(max(n, 1) * h * a, dtype=torch.int32, device="cuda")
+    _lib.cem_sample(to_dev(mu), to_dev(sigma), n, seed, rnd, plan, -1.0, 1.0, x, raw)
+    torch.cuda.synchronize()
+    if n == 0:
+        return
+    words = to_np(raw).view(np.uint32)
+    np.testing.assert_array_equal(words, o_sampler.raw_words(seed, rnd, plan, n * h * a))
+    want = o_sampler.sample_actions(mu, sigma, seed, rnd, plan, n, -1.0, 1.0)
+    got = to_np(x)[:n]
+    # float64 libm differences can move z by one float32 ulp in rare cases: count them
+    diff = got != want
+    ulps = np.abs(got.view(np.int32).astype(np.int64) - want.view(np.int32).astype(np.int64))
+    log(f"  sampler mismatches: {int(diff.sum())} of {got.size}")
+    assert ulps.max() <= 1
+    assert diff.sum() <= max(2, got.size // 100000)
+
+
+def _energies_with_specials(rng, n):
+    e = rng.standard_normal(n).astype(np.float32)
+    if n >= 16:
+        e[rng.integers(0, n, 4)] = np.nan
+        e[rng.integers(0, n, 3)] = np.inf
+        e[rng.integers(0, n, 3)] = -np.inf
+        e[rng.integers(0, n, 3)] = -0.0
+        e[rng.integers(0, n, 3)] = 0.0
+        e[rng.integers(0, n, n // 4)] = 0.5   # many ties
+    return e
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (7, 3), (64, 8), (800, 80), (801, 800), (3200, 320),
+                                 (16384, 1638), (1000, 1000)])
+def test_topk_bit_exact(gpu_lib, n, k):
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    log(f"topk n={n} k={k}")
+    e = _energies_with_specials(np.random.default_rng(n), n)
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    _lib.topk_select(to_dev(e), k, idx)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(idx), o_select.topk_elites(e, k))
+
+
+@pytest.mark.parametrize("n,k,h", [(800, 80, 1), (256, 32, 3), (3200, 320, 1), (9, 9, 4), (5, 1, 2)])
+def test_elite_refit_matches_oracle(gpu_lib, n, k, h):
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    log(f"elite_refit n={n} k={k} h={h}")
+    rng = np.random.default_rng(n * 7 + k)
+    e = _energies_with_specials(rng, n)
+    x = np.clip(rng.standard_normal((n, h, 7)), -1, 1).astype(np.float32)
+    idx = torch.empty(k, dtype=torch.int32, device="cuda")
+    mu = torch.empty((h, 7), dtype=torch.float32, device="cuda")
+    sg = torch.empty((h, 7), dtype=torch.float32, device="cuda")
+    _lib.elite_refit(to_dev(e), to_dev(x), k, idx, mu, sg)
+    torch.cuda.synchronize()
+    want_idx = o_select.topk_elites(e, k)
+    np.testing.assert_array_equal(to_np(idx), want_idx)
+    want_mu, want_sg = o_refit.refit(x, want_idx)
+    np.testing.assert_allclose(to_np(mu), want_mu, rtol=2e-7, atol=1e-7)
+    np.testing.assert_allclose(to_np(sg), want_sg, rtol=2e-7, atol=1e-7)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("n,p,e", [(5, 16, 128), (3, 7, 9), (64, 66, 512), (0, 4, 8)])
+def test_energy_l1_matches_oracle(gpu_lib, dtype, n, p, e):
+    import torch
+    from cem_jepa_predictor_amd import _lib, inputs
+
+    log(f"energy {dtype} n={n} p={p} e={e}")
+    zp, zg = inputs.make_predictions(max(n, 1), p, e, seed=n + p)
+    tz = to_dev(zp[:n] if n else zp[:1])
+    if dtype == "bf16":
+        tz = tz.to(torch.bfloat16)
+    out = torch.full((max(n, 1),), -1.0, dtype=torch.float32, device="cuda")
+    _lib.load().energy_l1(tz.data_ptr(), 1 if dtype == "bf16" else 0, to_dev(zg).data_ptr(), n, p, e,
+                          out.data_ptr(), None)
+    torch.cuda.synchronize()
+    if n == 0:
+        assert to_np(out)[0] == -1.0
+        return
+    want = o_energy.energy_l1(to_np(tz).reshape(n, p, e), zg)
+    np.testing.assert_allclose(to_np(out), want, rtol=2e-5, atol=0)
+
+
+def test_energy_l1_full_size_sampled(gpu_lib):
+    """N=800 candidates of [256, 1408] bf16 predictions, oracle on a sample of rows."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    log("energy full size 800 x 256 x 1408 bf16")
+    g = torch.Generator(device="cuda").manual_seed(0)
+    zp = torch.randn((800, 256, 1408), generator=g, device="cuda").to(torch.bfloat16)
+    zg = torch.randn((256, 1408), generator=g, device="cuda")
+    out = torch.empty(800, dtype=torch.float32, device="cuda")
+    _lib.energy_l1(zp, zg, out)
+    torch.cuda.synchronize()
+    rows = np.arange(0, 800, 53)
+    want = o_energy.energy_l1(zp[rows].float().cpu().numpy(), zg.cpu().numpy())
+    np.testing.assert_allclose(to_np(out)[rows], want, rtol=2e-5, atol=0)

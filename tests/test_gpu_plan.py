@@ -1,0 +1,211 @@
+"""GPU parity of the predictor rollout and of the full CEM plan step against the oracle.
+
+Modes (tolerances from the method's stated bar):
+  * rollout / energy parity: on the same candidate actions, GPU energies vs the
+    oracle's float64 energies, max relative error <= 1e-5 for the fp32 model and
+    <= 2e-2 for bf16 models;
+  * lockstep plan: the oracle runs its own sampler and refit but takes each
+    round's elites from the GPU's energies; elite lists must be bit-exact every
+    round and the final action within 1e-2 absolute;
+  * determinism: graph replay, direct enqueue and repeated runs are bitwise
+    identical, and so is any split of the candidates into launches.
+"""
+import numpy as np
+import pytest
+
+from oracle import energy as o_energy
+from oracle import refit as o_refit
+from oracle import sampler as o_sampler
+from oracle import select as o_select
+
+from .gpu_util import (gpu_model, log, max_rel, oracle_predictor, release_models, run_plan, to_dev,
+                       to_np, workload_data)
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _free_models():
+    yield
+    release_models()
+
+
+def gpu_rollout(name, actions):
+    import torch
+
+    wl, _, _, z_obs, _, s0 = workload_data(name)
+    m = wl.model
+    model = gpu_model(name)
+    dt = torch.bfloat16 if m.dtype == "bf16" else torch.float32
+    zp = torch.empty((actions.shape[0], m.patches, m.enc_dim), dtype=dt, device="cuda")
+    model.rollout(to_dev(actions), to_dev(z_obs), to_dev(s0), zp)
+    torch.cuda.synchronize()
+    return to_np(zp)
+
+
+@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12)])
+def test_rollout_matches_oracle(gpu_lib, name, n):
+    from cem_jepa_predictor_amd import inputs
+
+    wl, _, _, z_obs, z_goal, s0 = workload_data(name)
+    log(f"rollout {name} n={n} H={wl.plan.horizon}")
+    actions = inputs.make_actions(n, wl.plan.horizon, seed=n)
+    got = gpu_rollout(name, actions)
+    pred = oracle_predictor(name)
+    want = pred.rollout_cached(actions, z_obs, s0)
+    e_got = o_energy.energy_l1(got, z_goal)
+    e_want = o_energy.energy_l1(want, z_goal)
+    rel = max_rel(e_got, e_want)
+    scale = np.abs(want).max()
+    log(f"  energy max rel err {rel:.3e}; z max abs err {np.abs(got - want).max():.3e} (scale {scale:.2f})")
+    assert rel <= TOL[wl.model.dtype]
+    ztol = 1e-4 if wl.model.dtype == "f32" else 5e-2
+    assert np.abs(got - want).max() <= ztol * scale
+
+
+def _lockstep(name, out, oracle_rows):
+    """Follow the GPU plan round by round with the oracle."""
+    wl, _, _, z_obs, z_goal, s0 = workload_data(name)
+    pc = wl.plan
+    N, K, R, H = out["N"], out["K"], out["R"], out["H"]
+    pred = oracle_predictor(name)
+    mu = np.full((H, 7), pc.mu0, np.float32)
+    sigma = np.full((H, 7), pc.sigma0, np.float32)
+    worst = 0.0
+    for r in range(R):
+        x = o_sampler.sample_actions(mu, sigma, pc.seed, r, pc.plan_id, N, pc.clamp_lo, pc.clamp_hi)
+        # samples: identical up to a float32 ulp where float64 libms differ
+        ulps = np.abs(out["x"][r].view(np.int32).astype(np.int64) - x.view(np.int32).astype(np.int64))
+        assert ulps.max() <= 1, f"round {r}: samples differ by {ulps.max()} ulp"
+        rows = oracle_rows(r, N)
+        if len(rows):
+            e_or = o_energy.energy_l1(pred.rollout_cached(out["x"][r][rows], z_obs, s0), z_goal)
+            rel = max_rel(out["energy"][r][rows], e_or)
+            worst = max(worst, rel)
+            assert rel <= TOL[wl.model.dtype], f"round {r}: energy rel err {rel:.3e}"
+        elites = o_select.topk_elites(out["energy"][r], K)
+        np.testing.assert_array_equal(out["elites"][r], elites, err_msg=f"round {r}")
+        mu, sigma = o_refit.refit(x, elites)
+        np.testing.assert_allclose(out["mu"][r + 1], mu, rtol=0, atol=1e-6)
+        np.testing.assert_allclose(out["sigma"][r + 1], sigma, rtol=0, atol=1e-6)
+    assert np.abs(out["action"] - mu[0]).max() <= 1e-2
+    np.testing.assert_array_equal(out["action"], out["mu"][0])
+    assert out["best"] == out["elites"][R - 1][0]
+    return worst
+
+
+def test_plan_tiny_lockstep_all_candidates(gpu_lib):
+    log("plan tiny lockstep, oracle energies for every candidate")
+    out = run_plan("tiny")
+    worst = _lockstep("tiny", out, lambda r, n: np.arange(n))
+    log(f"  worst energy rel err {worst:.3e}")
+
+
+def test_plan_tiny_independent(gpu_lib):
+    """fp32: the oracle's own end-to-end plan picks the same elites."""
+    from oracle import cem
+
+    wl, _, _, z_obs, z_goal, s0 = workload_data("tiny")
+    pc = wl.plan
+    log("plan tiny independent")
+    out = run_plan("tiny")
+    pred = oracle_predictor("tiny")
+    ref = cem.cem_plan(cem.predictor_energy_fn(pred, z_obs, z_goal, s0), pc.n_samples, pc.n_elites,
+                       pc.rounds, np.full((pc.horizon, 7), pc.mu0), np.full((pc.horizon, 7), pc.sigma0),
+                       pc.seed, pc.plan_id, pc.clamp_lo, pc.clamp_hi)
+    for r in range(pc.rounds):
+        gaps = np.diff(np.sort(ref["trace"]["energy"][r]))
+        log(f"  round {r}: min energy gap {gaps.min():.3e}")
+        np.testing.assert_array_equal(out["elites"][r], ref["trace"]["elites"][r])
+    assert np.abs(out["action"] - ref["action"]).max() <= 1e-2
+
+
+def test_plan_small_lockstep_sampled(gpu_lib):
+    log("plan small lockstep, 6 oracle candidates per round")
+    out = run_plan("small")
+    worst = _lockstep("small", out, lambda r, n: np.random.default_rng(r).choice(n, 6, replace=False))
+    log(f"  worst energy rel err {worst:.3e}")
+
+
+def test_plan_vjepa2ac_full_size_lockstep(gpu_lib):
+    """The measured configuration: 800 candidates x 10 rounds, V-JEPA2-AC-shaped predictor."""
+    log("plan vjepa2ac full size (N=800, K=80, R=10, H=1) lockstep, oracle on 2 rounds x 2 candidates")
+    out = run_plan("vjepa2ac")
+    e = out["energy"]
+    spread = float(np.median(e.std(axis=1)))
+    log(f"  energy median {np.median(e):.5f}, per-round std median {spread:.3e}")
+    rows = {0: [0, 517], 9: [3, 799]}
+    worst = _lockstep("vjepa2ac", out, lambda r, n: np.array(rows.get(r, []), dtype=int))
+    log(f"  worst energy rel err {worst:.3e}")
+
+
+def test_plan_h4_kv_cache_lockstep(gpu_lib):
+    """Horizon 4 with the KV cache across frame blocks at full candidate count (2 rounds)."""
+    log("plan vjepa2ac_h4 (N=800, H=4) 2 rounds lockstep, oracle on 1 candidate per round")
+    out = run_plan("vjepa2ac_h4", rounds=2)
+    worst = _lockstep("vjepa2ac_h4", out, lambda r, n: np.array([7 + 400 * r]))
+    log(f"  worst energy rel err {worst:.3e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "small"])
+def test_plan_graph_equals_eager_and_is_deterministic(gpu_lib, name):
+    log(f"determinism {name}")
+    a = run_plan(name, use_graph=True)
+    b = run_plan(name, use_graph=False)
+    c = run_plan(name, use_graph=True)
+    for key in ["x", "energy", "elites", "mu", "sigma", "action"]:
+        np.testing.assert_array_equal(a[key], b[key], err_msg=key)
+        np.testing.assert_array_equal(a[key], c[key], err_msg=key)
+    # a different plan id draws different candidates
+    d = run_plan(name, plan_id=5)
+    assert not np.array_equal(a["x"], d["x"])
+
+
+def test_rollout_is_invariant_to_candidate_chunking(gpu_lib):
+    """Same seeds give the same answer however candidates are grouped (cf. plans identical
+    at 1, 2, 4 and 8 GPUs)."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    name = "small"
+    wl, _, _, z_obs, z_goal, s0 = workload_data(name)
+    from cem_jepa_predictor_amd import inputs
+
+    actions = inputs.make_actions(64, wl.plan.horizon, seed=11)
+    full = gpu_rollout(name, actions)
+    parts = np.concatenate([gpu_rollout(name, actions[i:i + 16]) for i in range(0, 64, 16)])
+    np.testing.assert_array_equal(full, parts)
+    e = torch.empty(64, dtype=torch.float32, device="cuda")
+    _lib.energy_l1(to_dev(full).to(torch.bfloat16), to_dev(z_goal), e)
+    torch.cuda.synchronize()
+
+
+def test_plan_energies_equal_rollout_then_energy(gpu_lib):
+    """The plan's fused round equals the stand-alone rollout + energy calls on its samples."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    name = "small"
+    wl, _, _, z_obs, z_goal, s0 = workload_data(name)
+    out = run_plan(name, rounds=2)
+    z = gpu_rollout(name, out["x"][1])
+    tz = to_dev(z).to(torch.bfloat16)
+    e = torch.empty(out["N"], dtype=torch.float32, device="cuda")
+    _lib.energy_l1(tz, to_dev(z_goal), e)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(e), out["energy"][1])
+
+
+@pytest.mark.parametrize("n,k,r", [(1, 1, 1), (17, 17, 2), (33, 5, 1)])
+def test_plan_edge_shapes(gpu_lib, n, k, r):
+    log(f"plan tiny edge N={n} K={k} R={r}")
+    out = run_plan("tiny", n=n, k=k, rounds=r)
+    _lockstep("tiny", out, lambda rr, nn: np.arange(nn))
+
+
+def test_plan_shorter_horizon_than_max(gpu_lib):
+    log("plan small with H=1 on a max-horizon-3 model")
+    out = run_plan("small", horizon=1, rounds=2)
+    _lockstep("small", out, lambda r, n: np.arange(4))
