@@ -7,16 +7,18 @@
 // block attention is bidirectional.  Softmax scale 1/sqrt(dh), fp32 softmax.
 //
 // bf16 kernel (dh = 64), one 256-thread workgroup per (candidate, head):
-//  * keys/values are staged through LDS in chunks of 64 keys: K row-major
-//    (16-byte chunks XOR-swizzled by key % 8) and V transposed (Vt[dh][key],
-//    padded rows) so that both MFMA operands are contiguous LDS reads;
-//  * each wave owns query tiles of 16 rows and computes S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 (lane l holds 16 scores of query l % 16), then an
-//    online (running max / running sum) softmax in fp32, then
+//  * the keys/values of one frame block at a time (B keys, padded to a
+//    multiple of 32) are staged in dynamic LDS: K row-major with 16-byte
+//    chunks XOR-swizzled by key % 8, V transposed (Vt[dh][key], padded rows) so
+//    both MFMA operands are contiguous LDS reads.  74 KB at B = 258, so two
+//    workgroups share a CU and one's loads overlap the other's math;
+//  * each wave owns 16-row query tiles and computes S^T = K Q^T with
+//    v_mfma_f32_16x16x32_bf16 (lane l holds scores of query l % 16), an online
+//    (running max / running sum) fp32 softmax over 64-key groups, then
 //    O^T += V^T P^T with P taken straight from registers: the MFMA sums over
 //    its 32 key slots, and the key each slot stands for is chosen so that the
-//    lane's own scores and the matching V^T entries line up (any consistent
-//    assignment of keys to slots gives the same sum);
+//    lane's own probabilities and the matching V^T entries line up (any
+//    consistent assignment of keys to slots gives the same sum);
 //  * HBM traffic per (candidate, head) is one read of Q, K, V and one write of
 //    O: the kernel is bandwidth-bound at the V-JEPA2-AC shape.
 #include "kernels.hpp"
@@ -25,9 +27,13 @@ namespace cem {
 namespace {
 
 constexpr int kDh = 64;
-constexpr int kChunk = 64;           // keys per LDS chunk
-constexpr int kVtLd = kChunk + 8;    // padded Vt row (bf16 elements)
 constexpr int kMaxTilesPerWave = 5;  // 16-row query tiles per wave -> B <= 320
+
+__host__ __device__ __forceinline__ int kpad_of(int B) { return (B + 31) & ~31; }
+__host__ __device__ __forceinline__ int vt_ld_of(int B) { return kpad_of(B) + 8; }
+__host__ __device__ __forceinline__ int lds_bytes_of(int B) {
+  return kpad_of(B) * kDh * 2 + kDh * vt_ld_of(B) * 2;
+}
 
 __device__ __forceinline__ float wave_max_q(float v) {
   // lanes l, l^16, l^32, l^48 share query l % 16
@@ -41,17 +47,14 @@ __device__ __forceinline__ float wave_sum_q(float v) {
   return v;
 }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-}
-
 __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs p) {
-  __shared__ __attribute__((aligned(16))) uint8_t k_lds[kChunk * kDh * 2];
-  __shared__ __attribute__((aligned(16))) bf16 vt_lds[kDh * kVtLd];
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int B = p.B, kpad = kpad_of(B), vld = vt_ld_of(B);
+  uint8_t* k_lds = lds;
+  bf16* vt_lds = reinterpret_cast<bf16*>(lds + kpad * kDh * 2);
 
   const int n = blockIdx.x / p.heads, h = blockIdx.x % p.heads;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int B = p.B, Lk = p.nblk * B;
   const int q_tiles = (B + 15) / 16;
   const int g = lane >> 4, ql = lane & 15;
   const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
@@ -75,86 +78,93 @@ __global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs p) {
     for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int n_chunks = (Lk + kChunk - 1) / kChunk;
-  for (int c = 0; c < n_chunks; ++c) {
-    // ---- stage 64 keys: 512 16-byte pieces of K and of V, two per thread
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int item = tid + 256 * it;
+  for (int blk = 0; blk < p.nblk; ++blk) {
+    const bf16* kvb = static_cast<const bf16*>(p.kv[blk]) + (long long)n * B * p.ldkv + h * kDh;
+    // ---- K: 8 lanes per 128-byte key row (coalesced), 16-byte swizzled LDS stores
+    for (int item = tid; item < kpad * 8; item += 256) {
       const int kr = item >> 3, ck = item & 7;
-      const int key = min(c * kChunk + kr, Lk - 1);
-      const int blk = key / B, row = key - blk * B;
-      const bf16* src = static_cast<const bf16*>(p.kv[blk]) + ((long long)n * B + row) * p.ldkv +
-                        h * kDh + ck * 8;
-      const uint4 kv = *reinterpret_cast<const uint4*>(src);
-      const uint4 vv = *reinterpret_cast<const uint4*>(src + p.d);
-      *reinterpret_cast<uint4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = kv;
-      const bf16* ve = reinterpret_cast<const bf16*>(&vv);
+      const uint4 v = *reinterpret_cast<const uint4*>(kvb + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
+      *reinterpret_cast<uint4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = v;
+    }
+    // ---- V: a wave takes 16 keys x 4 chunks, so each transposed 2-byte store
+    // instruction writes 4 Vt rows x 32 contiguous bytes on distinct banks
+    for (int item = tid; item < kpad * 8; item += 256) {
+      const int kr = (item & 15) + 16 * (item >> 7);
+      const int ck = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
+      const uint4 v = *reinterpret_cast<const uint4*>(kvb + p.d + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
+      const bf16* ve = reinterpret_cast<const bf16*>(&v);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) vt_lds[(ck * 8 + e) * kVtLd + kr] = ve[e];
+      for (int e = 0; e < 8; ++e) vt_lds[(ck * 8 + e) * vld + kr] = ve[e];
     }
     __syncthreads();
 
-    const int valid = Lk - c * kChunk;   // keys >= valid in this chunk are padding
 #pragma unroll
     for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
       const int tile = wave + 4 * ti;
       if (tile >= q_tiles) break;
-      // S^T[key][q] for the chunk's 4 key tiles: lane holds keys 16 kt + 4 g + r, query ql
-      f32x4_t st[4];
+      for (int g0 = 0; g0 < kpad; g0 += 64) {
+        const int nkt = min(4, (kpad - g0) >> 4);   // 4, or 2 in a trailing 32-key group
+        const int valid = B - g0;                   // keys >= valid are padding
+        // S^T[key][q]: lane holds keys g0 + 16 kt + 4 g + r of query ql
+        f32x4_t st[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int kr = kt * 16 + ql;
+        for (int kt = 0; kt < 4; ++kt) {
+          st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          if (kt < nkt) {
+            const int kr = g0 + kt * 16 + ql;
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
-          st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ti][s], st[kt], 0, 0, 0);
+            for (int s = 0; s < 2; ++s) {
+              const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+                  k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
+              st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ti][s], st[kt], 0, 0, 0);
+            }
+          }
         }
-      }
-      float cmax = -INFINITY;
+        float cmax = -INFINITY;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = kt * 16 + 4 * g + r;
-          const float v = (key < valid) ? st[kt][r] * sl2 : -INFINITY;
-          st[kt][r] = v;
-          cmax = fmaxf(cmax, v);
-        }
-      cmax = wave_max_q(cmax);
-      const float mnew = fmaxf(mrun[ti], cmax);      // finite: every chunk has a valid key
-      const float alpha = exp2f(mrun[ti] - mnew);    // exp2(-inf) = 0 on the first chunk
-      mrun[ti] = mnew;
-      float psum = 0.f;
+          for (int r = 0; r < 4; ++r) {
+            const int key = kt * 16 + 4 * g + r;
+            const float v = (kt < nkt && key < valid) ? st[kt][r] * sl2 : -INFINITY;
+            st[kt][r] = v;
+            cmax = fmaxf(cmax, v);
+          }
+        cmax = wave_max_q(cmax);
+        const float mnew = fmaxf(mrun[ti], cmax);      // finite: every group has a valid key
+        const float alpha = exp2f(mrun[ti] - mnew);    // exp2(-inf) = 0 on the first group
+        mrun[ti] = mnew;
+        float psum = 0.f;
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
+        for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = exp2f(st[kt][r] - mnew);
-          st[kt][r] = e;
-          psum += e;
-        }
-      lrun[ti] = lrun[ti] * alpha + psum;
+          for (int r = 0; r < 4; ++r) {
+            const float e = exp2f(st[kt][r] - mnew);
+            st[kt][r] = e;
+            psum += e;
+          }
+        lrun[ti] = lrun[ti] * alpha + psum;
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] *= alpha;
-      // O^T[dh][q] += V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
-      // 32 sg + 4 g + e (e < 4) or 32 sg + 16 + 4 g + (e - 4) (e >= 4)
+        for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] *= alpha;
+        // O^T[dh][q] += V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
+        // g0 + 32 sg + 4 g + e (e < 4) or g0 + 32 sg + 16 + 4 g + (e - 4) (e >= 4)
 #pragma unroll
-      for (int sg = 0; sg < 2; ++sg) {
-        union { uint32_t u[4]; bf16x8_t v; } pf;
-        pf.u[0] = pack_bf16x2(st[2 * sg][0], st[2 * sg][1]);
-        pf.u[1] = pack_bf16x2(st[2 * sg][2], st[2 * sg][3]);
-        pf.u[2] = pack_bf16x2(st[2 * sg + 1][0], st[2 * sg + 1][1]);
-        pf.u[3] = pack_bf16x2(st[2 * sg + 1][2], st[2 * sg + 1][3]);
+        for (int sg = 0; sg < 2; ++sg) {
+          if (2 * sg < nkt) {
+            union { uint32_t u[4]; bf16x8_t v; } pf;
+            pf.u[0] = pack_bf16x2(st[2 * sg][0], st[2 * sg][1]);
+            pf.u[1] = pack_bf16x2(st[2 * sg][2], st[2 * sg][3]);
+            pf.u[2] = pack_bf16x2(st[2 * sg + 1][0], st[2 * sg + 1][1]);
+            pf.u[3] = pack_bf16x2(st[2 * sg + 1][2], st[2 * sg + 1][3]);
 #pragma unroll
-        for (int dt = 0; dt < 4; ++dt) {
-          const bf16* vrow = vt_lds + (dt * 16 + ql) * kVtLd + 32 * sg + 4 * g;
-          union { uint2 u[2]; bf16x8_t v; } vf;
-          vf.u[0] = *reinterpret_cast<const uint2*>(vrow);
-          vf.u[1] = *reinterpret_cast<const uint2*>(vrow + 16);
-          oacc[ti][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[ti][dt], 0, 0, 0);
+            for (int dt = 0; dt < 4; ++dt) {
+              const bf16* vrow = vt_lds + (dt * 16 + ql) * vld + g0 + 32 * sg + 4 * g;
+              union { uint2 u[2]; bf16x8_t v; } vf;
+              vf.u[0] = *reinterpret_cast<const uint2*>(vrow);
+              vf.u[1] = *reinterpret_cast<const uint2*>(vrow + 16);
+              oacc[ti][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[ti][dt], 0, 0, 0);
+            }
+          }
         }
       }
     }
@@ -224,9 +234,15 @@ bool attention_bf16_supports(int dh, int B) {
 }
 bool attention_f32_supports(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
+hipError_t attention_init() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             lds_bytes_of(16 * 4 * kMaxTilesPerWave));
+}
+
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.n <= 0) return hipSuccess;
-  attn_bf16_kernel<<<a.n * a.heads, 256, 0, stream>>>(a);
+  attn_bf16_kernel<<<a.n * a.heads, 256, lds_bytes_of(a.B), stream>>>(a);
   return hipGetLastError();
 }
 

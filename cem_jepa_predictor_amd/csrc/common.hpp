@@ -9,6 +9,8 @@ namespace cem {
 using bf16 = uint16_t;   // storage type: upper 16 bits of an IEEE binary32
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
@@ -16,12 +18,15 @@ __device__ __forceinline__ float bf16_to_f32(bf16 v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// Round to nearest, ties to even (finite inputs; NaN stays NaN).
+// Two floats -> packed bf16 pair (low half = a), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const bf16x2_t v = __builtin_convertvector(f32x2_t{a, b}, bf16x2_t);
+  return __builtin_bit_cast(uint32_t, v);
+}
+// Round to nearest, ties to even.
 __device__ __forceinline__ bf16 f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u) return static_cast<bf16>((u >> 16) | ((u & 0xffffu) ? 0x40u : 0u));
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16>(u >> 16);
+  return static_cast<bf16>(pack_bf16x2(f, 0.f) & 0xffffu);
 }
 
 template <typename T> struct Elem;
@@ -64,8 +69,25 @@ struct Epilogue {
 
 enum class Act { None, Gelu };
 
+// GELU(x) = x * Phi(x) with Phi from the exact erf (libm erff): fp32 models.
 __device__ __forceinline__ float gelu_exact(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
+}
+
+// GELU(x) = x * Phi(x) for bf16 models, branch-free.  Phi(-|x|) = erfc(z) / 2 with
+// z = |x| / sqrt(2) and erfc(z) ~= t (a1 + a2 t + ... + a5 t^4) exp(-z^2),
+// t = 1 / (1 + p z): Abramowitz & Stegun, Handbook of Mathematical Functions,
+// eq. 7.1.26 (Hastings), |erf error| <= 1.5e-7 -- four orders of magnitude
+// below the bf16 rounding applied to the result.
+__device__ __forceinline__ float gelu_bf16_path(float x) {
+  const float z = fabsf(x) * 0.70710678118654752440f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
+  float poly = fmaf(t, 1.061405429f, -1.453152027f);
+  poly = fmaf(t, poly, 1.421413741f);
+  poly = fmaf(t, poly, -0.284496736f);
+  poly = fmaf(t, poly, 0.254829592f);
+  const float h = 0.5f * t * poly * __expf(-z * z);   // Phi(-|x|)
+  return x * (x >= 0.f ? 1.0f - h : h);
 }
 
 }  // namespace cem

@@ -29,7 +29,7 @@
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
 //    each carries only its own epilogue code.
 //
-// Epilogue (fp32): + bias, optional exact GELU, optional residual add (the
+// Epilogue (fp32): + bias, optional GELU, optional residual add (the
 // output already holds the residual stream), optional column split into two
 // destinations (q -> Q buffer, k|v -> KV cache), optional output-row remap.
 #include "kernels.hpp"
@@ -47,10 +47,11 @@ template <> struct Store4<bf16> {
   }
   __device__ static __forceinline__ void store(bf16* p, const float v[4]) {
     uint2 u;
-    u.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-    u.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    u.x = pack_bf16x2(v[0], v[1]);
+    u.y = pack_bf16x2(v[2], v[3]);
     *reinterpret_cast<uint2*>(p) = u;
   }
+  __device__ static __forceinline__ float gelu(float x) { return gelu_bf16_path(x); }
 };
 template <> struct Store4<float> {
   __device__ static __forceinline__ void load(const float* p, float v[4]) {
@@ -60,6 +61,7 @@ template <> struct Store4<float> {
   __device__ static __forceinline__ void store(float* p, const float v[4]) {
     *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
   }
+  __device__ static __forceinline__ float gelu(float x) { return gelu_exact(x); }
 };
 
 // Four consecutive output columns n..n+3 (n % 4 == 0, N % 4 == 0) of the
@@ -76,7 +78,7 @@ __device__ __forceinline__ void epilogue_row4(const Epilogue& e, int N, long lon
   }
   if constexpr (KIND == kEpiGelu) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = gelu_exact(v[i]);
+    for (int i = 0; i < 4; ++i) v[i] = Store4<T>::gelu(v[i]);
   }
   T* p = (n < e.split) ? static_cast<T*>(e.c0) + row * e.ld0 + n
                        : static_cast<T*>(e.c1) + row * e.ld1 + (n - e.split);

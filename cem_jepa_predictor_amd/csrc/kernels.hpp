@@ -62,6 +62,7 @@ struct AttnArgs {
   float scale;
 };
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
+hipError_t attention_init();   // one-time dynamic-LDS attribute
 hipError_t launch_attention_f32(const AttnArgs& a, hipStream_t stream);
 bool attention_bf16_supports(int dh, int B);
 bool attention_f32_supports(int dh);

@@ -26,9 +26,7 @@ template <> struct Pair<bf16> {
     a = __uint_as_float(v << 16);
     b = __uint_as_float(v & 0xffff0000u);
   }
-  __device__ static __forceinline__ V pack(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
-  }
+  __device__ static __forceinline__ V pack(float a, float b) { return pack_bf16x2(a, b); }
 };
 
 __device__ __forceinline__ float wave_sum(float v) {

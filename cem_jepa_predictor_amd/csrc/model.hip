@@ -225,6 +225,8 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   if (e != hipSuccess) return fail(hip_status(e, "select_init"));
   e = gemm_init();
   if (e != hipSuccess) return fail(hip_status(e, "gemm_init"));
+  e = attention_init();
+  if (e != hipSuccess) return fail(hip_status(e, "attention_init"));
   e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) return fail(hip_status(e, "hipStreamCreate"));
   *out = m;

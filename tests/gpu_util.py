@@ -89,8 +89,9 @@ def run_plan(name: str, *, use_graph: bool = True, rounds: int | None = None,
         "sigma": model.trace(_lib.TRACE_SIGMA, torch.empty((R + 1, H, A), dtype=torch.float32, device="cuda")),
     }
     torch.cuda.synchronize()
-    out = {"action": to_np(action), "mu": to_np(mu), "sigma": to_np(sigma), "best": int(best.item())}
-    out.update({k2: to_np(v) for k2, v in tr.items()})
+    out = {"action": to_np(action), "mu_out": to_np(mu), "sigma_out": to_np(sigma),
+           "best": int(best.item())}
+    out.update({k2: to_np(v) for k2, v in tr.items()})   # "mu"/"sigma" are the per-round history
     out.update(N=N, K=K, R=R, H=H)
     return out
 

@@ -116,12 +116,43 @@ def test_energy_l1_full_size_sampled(gpu_lib):
     from cem_jepa_predictor_amd import _lib
 
     log("energy full size 800 x 256 x 1408 bf16")
-    g = torch.Generator(device="cuda").manual_seed(0)
-    zp = torch.randn((800, 256, 1408), generator=g, device="cuda").to(torch.bfloat16)
-    zg = torch.randn((256, 1408), generator=g, device="cuda")
+    rng = np.random.default_rng(0)
+    zp_h = rng.standard_normal((800, 256, 1408), dtype=np.float32)
+    zg_h = rng.standard_normal((256, 1408), dtype=np.float32)
+    zp = to_dev(zp_h).to(torch.bfloat16)
+    zg = to_dev(zg_h)
+    torch.cuda.synchronize()
     out = torch.empty(800, dtype=torch.float32, device="cuda")
     _lib.energy_l1(zp, zg, out)
     torch.cuda.synchronize()
+    got = to_np(out)
+    ref_t = (zp.float() - zg).abs().mean(dim=(1, 2))
+    torch.cuda.synchronize()
+    log(f"  nan rows {int(np.isnan(got).sum())}, max |ours - torch| {np.nanmax(np.abs(got - to_np(ref_t))):.3e}, "
+        f"stream {torch.cuda.current_stream().cuda_stream}")
     rows = np.arange(0, 800, 53)
-    want = o_energy.energy_l1(zp[rows].float().cpu().numpy(), zg.cpu().numpy())
-    np.testing.assert_allclose(to_np(out)[rows], want, rtol=2e-5, atol=0)
+    want = o_energy.energy_l1(zp[rows].float().cpu().numpy(), zg_h)
+    np.testing.assert_allclose(got[rows], want, rtol=2e-5, atol=0)
+    # deterministic on a second call
+    _lib.energy_l1(zp, zg, out)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(to_np(out), got)
+
+
+def test_energy_l1_device_generated_inputs(gpu_lib):
+    """Inputs produced by device kernels right before the call (stream ordering)."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    log("energy with torch.randn inputs on the device")
+    g = torch.Generator(device="cuda").manual_seed(0)
+    zp = torch.randn((800, 256, 1408), generator=g, device="cuda").to(torch.bfloat16)
+    zg = torch.randn((256, 1408), generator=g, device="cuda")
+    out = torch.full((800,), -7.0, dtype=torch.float32, device="cuda")
+    _lib.energy_l1(zp, zg, out)
+    ref = (zp.float() - zg).abs().mean(dim=(1, 2))
+    torch.cuda.synchronize()
+    got, want = to_np(out), to_np(ref)
+    log(f"  ours: nan {int(np.isnan(got).sum())}, untouched {int((got == -7.0).sum())}; "
+        f"torch: nan {int(np.isnan(want).sum())}; inputs finite {bool(torch.isfinite(zp).all())}")
+    np.testing.assert_allclose(got, want, rtol=2e-5, atol=0)

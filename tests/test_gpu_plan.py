@@ -91,7 +91,9 @@ def _lockstep(name, out, oracle_rows):
         np.testing.assert_allclose(out["mu"][r + 1], mu, rtol=0, atol=1e-6)
         np.testing.assert_allclose(out["sigma"][r + 1], sigma, rtol=0, atol=1e-6)
     assert np.abs(out["action"] - mu[0]).max() <= 1e-2
-    np.testing.assert_array_equal(out["action"], out["mu"][0])
+    np.testing.assert_array_equal(out["action"], out["mu"][R][0])
+    np.testing.assert_array_equal(out["mu_out"], out["mu"][R])
+    np.testing.assert_array_equal(out["sigma_out"], out["sigma"][R])
     assert out["best"] == out["elites"][R - 1][0]
     return worst
 
