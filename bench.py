@@ -94,6 +94,9 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timers", action="store_true")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration only: run a plain device copy of this many bytes 3 times "
+                         "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -111,6 +114,14 @@ def main() -> int:
         eprint("no GPU available")
         return 1
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        src = torch.ones(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        eprint(f"[bench] copied {args.copy_bytes} bytes 3 times")
+        return 0
     if args.samples:
         wl = inputs.sweep_workload(args.samples)
     else:

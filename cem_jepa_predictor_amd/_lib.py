@@ -99,11 +99,41 @@ def _ptr(t) -> Optional[int]:
     return t.data_ptr()
 
 
-def _stream(stream) -> Optional[int]:
-    import torch
+_side_streams = {}
 
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return s.cuda_stream or None
+
+class _OnStream:
+    """Run library calls on an explicit HIP stream ordered with torch's work.
+
+    An explicit torch stream with a real handle is used as is.  torch's default
+    stream reports handle 0, which the library would read as HIP's legacy null
+    stream -- not necessarily the stream torch launched its own kernels on.  So
+    library calls then go to a torch-created side stream that first waits for
+    torch's current stream, and torch's current stream waits for it afterwards.
+    """
+
+    def __init__(self, stream):
+        import torch
+
+        self.cur = stream if stream is not None else torch.cuda.current_stream()
+        self.side = None
+        if self.cur.cuda_stream == 0:
+            dev = self.cur.device
+            key = dev.index if dev.index is not None else torch.cuda.current_device()
+            if key not in _side_streams:
+                _side_streams[key] = torch.cuda.Stream(device=key)
+            self.side = _side_streams[key]
+
+    def __enter__(self) -> int:
+        if self.side is None:
+            return self.cur.cuda_stream
+        self.side.wait_stream(self.cur)
+        return self.side.cuda_stream
+
+    def __exit__(self, *exc):
+        if self.side is not None:
+            self.cur.wait_stream(self.side)
+        return False
 
 
 def model_desc(m: ModelConfig, max_samples: int, max_horizon: Optional[int] = None) -> ModelDesc:
@@ -149,19 +179,22 @@ class Model:
              clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True, stream=None):
         p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
                    1 if use_graph else 0)
-        _check(load().cem_plan(self.handle, ctypes.byref(p), _ptr(z_obs), _ptr(z_goal), _ptr(s0),
-                               _ptr(mu), _ptr(sigma), _ptr(action), _ptr(best_idx), _stream(stream)))
+        with _OnStream(stream) as st:
+            _check(load().cem_plan(self.handle, ctypes.byref(p), _ptr(z_obs), _ptr(z_goal), _ptr(s0),
+                                   _ptr(mu), _ptr(sigma), _ptr(action), _ptr(best_idx), st))
         self._last = p
 
     def trace(self, kind: int, out, stream=None):
-        _check(load().cem_plan_trace(self.handle, kind, _ptr(out), out.numel() * out.element_size(),
-                                     _stream(stream)))
+        with _OnStream(stream) as st:
+            _check(load().cem_plan_trace(self.handle, kind, _ptr(out), out.numel() * out.element_size(),
+                                         st))
         return out
 
     def rollout(self, actions, z_obs, s0, z_pred, stream=None):
         n, h = actions.shape[0], actions.shape[1]
-        _check(load().predictor_rollout(self.handle, _ptr(actions), n, h, _ptr(z_obs), _ptr(s0),
-                                        _ptr(z_pred), _stream(stream)))
+        with _OnStream(stream) as st:
+            _check(load().predictor_rollout(self.handle, _ptr(actions), n, h, _ptr(z_obs), _ptr(s0),
+                                            _ptr(z_pred), st))
         return z_pred
 
     def timer_enable(self, on: bool = True):
@@ -178,21 +211,25 @@ def energy_l1(z_pred, z_goal, energy, stream=None):
 
     dt = CEM_BF16 if z_pred.dtype == torch.bfloat16 else CEM_F32
     n, p, e = z_pred.shape
-    _check(load().energy_l1(_ptr(z_pred), dt, _ptr(z_goal), n, p, e, _ptr(energy), _stream(stream)))
+    with _OnStream(stream) as st:
+        _check(load().energy_l1(_ptr(z_pred), dt, _ptr(z_goal), n, p, e, _ptr(energy), st))
     return energy
 
 
 def elite_refit(energy, actions, k, elite_idx, mu, sigma, stream=None):
     n, h, a = actions.shape
-    _check(load().elite_refit(_ptr(energy), _ptr(actions), n, k, h, a, _ptr(elite_idx), _ptr(mu),
-                              _ptr(sigma), _stream(stream)))
+    with _OnStream(stream) as st:
+        _check(load().elite_refit(_ptr(energy), _ptr(actions), n, k, h, a, _ptr(elite_idx), _ptr(mu),
+                                  _ptr(sigma), st))
 
 
 def cem_sample(mu, sigma, n, seed, rnd, plan_id, lo, hi, actions, raw_words=None, stream=None):
     h, a = mu.shape
-    _check(load().cem_sample(_ptr(mu), _ptr(sigma), n, h, a, seed, rnd, plan_id, lo, hi,
-                             _ptr(actions), _ptr(raw_words), _stream(stream)))
+    with _OnStream(stream) as st:
+        _check(load().cem_sample(_ptr(mu), _ptr(sigma), n, h, a, seed, rnd, plan_id, lo, hi,
+                                 _ptr(actions), _ptr(raw_words), st))
 
 
 def topk_select(energy, k, idx, stream=None):
-    _check(load().topk_select(_ptr(energy), energy.numel(), k, _ptr(idx), _stream(stream)))
+    with _OnStream(stream) as st:
+        _check(load().topk_select(_ptr(energy), energy.numel(), k, _ptr(idx), st))

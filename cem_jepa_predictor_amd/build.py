@@ -27,6 +27,8 @@ ARCH = "gfx950"
 SOURCES = ["sampler.hip", "embed.hip", "layernorm.hip", "gemm.hip", "attention.hip",
            "energy.hip", "select_refit.hip", "model.hip", "abi.hip"]
 NO_CONTRACT = {"sampler.hip", "select_refit.hip"}
+# attention keeps its MFMA accumulators in VGPRs: its softmax rescales them with VALU ops
+EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def hipcc() -> str:
@@ -42,6 +44,7 @@ def _flags(src: str):
          "-I", INCLUDE, "-I", CSRC, "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
     if src in NO_CONTRACT:
         f.append("-ffp-contract=off")
+    f += EXTRA.get(src, [])
     return f
 
 

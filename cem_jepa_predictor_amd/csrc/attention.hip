@@ -12,15 +12,18 @@
 //    chunks XOR-swizzled by key % 8, V transposed (Vt[dh][key], padded rows) so
 //    both MFMA operands are contiguous LDS reads.  74 KB at B = 258, so two
 //    workgroups share a CU and one's loads overlap the other's math;
-//  * each wave owns 16-row query tiles and computes S^T = K Q^T with
-//    v_mfma_f32_16x16x32_bf16 (lane l holds scores of query l % 16), an online
-//    (running max / running sum) fp32 softmax over 64-key groups, then
+//  * each wave owns 16-row query tiles; per tile and staged block it computes
+//    all of S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane l holds the scores
+//    of query l % 16 in registers), takes the block's exact max, and keeps a
+//    running max / sum only across frame blocks (one rescale per block); then
 //    O^T += V^T P^T with P taken straight from registers: the MFMA sums over
 //    its 32 key slots, and the key each slot stands for is chosen so that the
 //    lane's own probabilities and the matching V^T entries line up (any
 //    consistent assignment of keys to slots gives the same sum);
 //  * HBM traffic per (candidate, head) is one read of Q, K, V and one write of
 //    O: the kernel is bandwidth-bound at the V-JEPA2-AC shape.
+#include <utility>
+
 #include "kernels.hpp"
 
 namespace cem {
@@ -28,6 +31,7 @@ namespace {
 
 constexpr int kDh = 64;
 constexpr int kMaxTilesPerWave = 5;  // 16-row query tiles per wave -> B <= 320
+constexpr int kMaxKeyTiles = 20;     // 16-key tiles per staged block -> B <= 320
 
 __host__ __device__ __forceinline__ int kpad_of(int B) { return (B + 31) & ~31; }
 __host__ __device__ __forceinline__ int vt_ld_of(int B) { return kpad_of(B) + 8; }
@@ -47,7 +51,126 @@ __device__ __forceinline__ float wave_sum_q(float v) {
   return v;
 }
 
-__global__ __launch_bounds__(256) void attn_bf16_kernel(AttnArgs p) {
+// One frame block (every query sees exactly the B keys of its own block):
+// each query tile computes its full score block in registers, takes the exact
+// max, exponentiates once and finishes before the next tile.
+// KT = ceil(B / 16): 16-key (and 16-query) tiles per block, fixed per model.
+template <int KT>
+__global__ __launch_bounds__(256) void attn_bf16_single_kernel(AttnArgs p) {
+  constexpr int kKT2 = 2 * ((KT + 1) / 2);   // key tiles rounded up to MFMA k = 32 pairs
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int B = p.B, kpad = kpad_of(B), vld = vt_ld_of(B);
+  uint8_t* k_lds = lds;
+  bf16* vt_lds = reinterpret_cast<bf16*>(lds + kpad * kDh * 2);
+
+  const int n = blockIdx.x / p.heads, h = blockIdx.x % p.heads;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, ql = lane & 15;
+  const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
+
+  const bf16* kvb = static_cast<const bf16*>(p.kv[0]) + (long long)n * B * p.ldkv + h * kDh;
+  // ---- K: 8 lanes per 128-byte key row (coalesced), 16-byte swizzled LDS stores
+  for (int item = tid; item < kpad * 8; item += 256) {
+    const int kr = item >> 3, ck = item & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(kvb + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
+    *reinterpret_cast<uint4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = v;
+  }
+  // ---- V: a wave takes 16 keys x 4 chunks, so each transposed 2-byte store
+  // instruction writes 4 Vt rows x 32 contiguous bytes on distinct banks
+  for (int item = tid; item < kpad * 8; item += 256) {
+    const int kr = (item & 15) + 16 * (item >> 7);
+    const int ck = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
+    const uint4 v = *reinterpret_cast<const uint4*>(kvb + p.d + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
+    const bf16* ve = reinterpret_cast<const bf16*>(&v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vt_lds[(ck * 8 + e) * vld + kr] = ve[e];
+  }
+  __syncthreads();
+
+  const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
+  bf16* obase = static_cast<bf16*>(p.o) + (long long)n * B * p.ldo + h * kDh;
+#pragma unroll 1
+  for (int tile = wave; tile < KT; tile += 4) {
+    const int qr = min(tile * 16 + ql, B - 1);
+    bf16x8_t qf[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qf[s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+    // S^T[key][q]: lane holds keys 16 kt + 4 g + r of query ql
+    f32x4_t st[kKT2];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < kKT2; ++kt) {
+      st[kt] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (kt < KT) {
+        const int kr = kt * 16 + ql;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+              k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // only the last key tile can hold padding keys
+          const float v = (kt < KT - 1 || kt * 16 + 4 * g + r < B) ? acc[r] * sl2 : -INFINITY;
+          st[kt][r] = v;
+          bmax = fmaxf(bmax, v);
+        }
+      }
+      // bound how many K fragments the scheduler keeps in flight (register pressure)
+      if ((kt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    bmax = wave_max_q(bmax);
+    float psum = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < kKT2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(st[kt][r] - bmax);
+        st[kt][r] = e;
+        psum += e;
+      }
+    // O^T[dh][q] = V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
+    // 32 sg + 4 g + e (e < 4) or 32 sg + 16 + 4 g + (e - 4) (e >= 4)
+    f32x4_t oacc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sg = 0; sg < kKT2 / 2; ++sg) {
+      union { uint32_t u[4]; bf16x8_t v; } pf;
+      pf.u[0] = pack_bf16x2(st[2 * sg][0], st[2 * sg][1]);
+      pf.u[1] = pack_bf16x2(st[2 * sg][2], st[2 * sg][3]);
+      pf.u[2] = pack_bf16x2(st[2 * sg + 1][0], st[2 * sg + 1][1]);
+      pf.u[3] = pack_bf16x2(st[2 * sg + 1][2], st[2 * sg + 1][3]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const bf16* vrow = vt_lds + (dt * 16 + ql) * vld + 32 * sg + 4 * g;
+        union { uint2 u[2]; bf16x8_t v; } vf;
+        vf.u[0] = *reinterpret_cast<const uint2*>(vrow);
+        vf.u[1] = *reinterpret_cast<const uint2*>(vrow + 16);
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[dt], 0, 0, 0);
+      }
+    }
+    // lane holds O[q = 16 tile + ql][dh = 16 dt + 4 g + r]
+    const float inv = 1.0f / wave_sum_q(psum);
+    const int q = tile * 16 + ql;
+    if (q < B) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        uint2 u;
+        u.x = pack_bf16x2(oacc[dt][0] * inv, oacc[dt][1] * inv);
+        u.y = pack_bf16x2(oacc[dt][2] * inv, oacc[dt][3] * inv);
+        *reinterpret_cast<uint2*>(obase + (long long)q * p.ldo + dt * 16 + 4 * g) = u;
+      }
+    }
+  }
+}
+
+// Several frame blocks (KV cache): an online (running max / sum) softmax over
+// 64-key groups, rescaling the O accumulators whenever the max grows.
+__global__ __launch_bounds__(256) void attn_bf16_multi_kernel(AttnArgs p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int B = p.B, kpad = kpad_of(B), vld = vt_ld_of(B);
   uint8_t* k_lds = lds;
@@ -234,15 +357,38 @@ bool attention_bf16_supports(int dh, int B) {
 }
 bool attention_f32_supports(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
+template <int KT>
+hipError_t set_lds_attr() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_single_kernel<KT>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes_of(16 * KT));
+}
+template <int... KTs>
+hipError_t set_all(std::integer_sequence<int, KTs...>) {
+  hipError_t e = hipSuccess;
+  ((e = (e == hipSuccess ? set_lds_attr<KTs + 1>() : e)), ...);
+  return e;
+}
+template <int... KTs>
+void launch_kt(int kt, const AttnArgs& a, hipStream_t stream, std::integer_sequence<int, KTs...>) {
+  ((kt == KTs + 1 ? (attn_bf16_single_kernel<KTs + 1><<<a.n * a.heads, 256, lds_bytes_of(a.B), stream>>>(a), 0) : 0), ...);
+}
+using KtRange = std::make_integer_sequence<int, kMaxKeyTiles>;
+
 hipError_t attention_init() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize,
-                             lds_bytes_of(16 * 4 * kMaxTilesPerWave));
+  const hipError_t e = set_all(KtRange{});
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_multi_kernel),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes_of(16 * kMaxKeyTiles));
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.n <= 0) return hipSuccess;
-  attn_bf16_kernel<<<a.n * a.heads, 256, lds_bytes_of(a.B), stream>>>(a);
+  const int kt = (a.B + 15) / 16;
+  if (kt < 1 || kt > kMaxKeyTiles) return hipErrorInvalidValue;
+  if (a.nblk == 1)
+    launch_kt(kt, a, stream, KtRange{});
+  else
+    attn_bf16_multi_kernel<<<a.n * a.heads, 256, lds_bytes_of(a.B), stream>>>(a);
   return hipGetLastError();
 }
 

@@ -15,11 +15,13 @@
 //    activation tile, so each lane's accumulator quads hold 4 consecutive
 //    output columns of one output row: the epilogue reads bias / residual and
 //    writes 8-byte (bf16) vectors.
-//  * LDS double buffer (2 x 64 KB): global -> registers -> LDS, with the next
-//    K-slab's global loads in flight during the current slab's MFMAs; one
-//    barrier per slab.  Rows of 64 bf16 (128 B) are stored as eight 16-byte
-//    chunks, chunk c of row r at position c ^ (r & 7), so the 32 rows a
-//    fragment read touches spread over all banks.
+//  * LDS double buffer (2 x 64 KB) filled by LDS-DMA buffer loads (global ->
+//    LDS without VGPRs), the slab after next in flight during the current
+//    slab's MFMAs; fragments double-buffered in registers so each substep's
+//    LDS reads overlap the previous substep's MFMAs; one barrier per slab,
+//    placed before the last substep's MFMAs.  Rows of 64 bf16 (128 B) are
+//    stored as eight 16-byte chunks, chunk c of row r at position
+//    c ^ ((r >> 1) & 7), so fragment reads are free of bank conflicts.
 //  * Block -> tile map is XCD-aware: the dispatcher hands block b to XCD
 //    b % 8, so each XCD receives a contiguous range of logical tiles, ordered
 //    in groups of 8 row-tiles to share A and B panels in that XCD's L2.
@@ -97,6 +99,8 @@ constexpr int TILE_BYTES = BM * BK * 2;       // 32 KB per operand slab
 constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // A slab + B slab
 constexpr int GROUP_M = 8;
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
 __device__ __forceinline__ void tile_of_block(int b, int nb, int tiles_m, int tiles_n, int& tm,
                                               int& tn) {
   const int xcd = b & 7, slot = b >> 3;
@@ -121,51 +125,53 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, in
       const_cast<bf16*>(base + (long long)row0 * ld + k), (short)0, (int)bytes, 0x00020000);
 }
 
+// Operand slabs go global -> LDS directly (buffer_load ... lds, 16 bytes per
+// lane at m0 + 16 * lane), so the data never occupies VGPRs.  Each wave
+// instruction fills 8 rows of 128 bytes; lane l loads row r = base + l / 8 and
+// the logical 16-byte chunk that belongs at LDS position l % 8 under the
+// swizzle.  Two stage arrays (distinct objects) let the compiler
+// see that DMA into one stage never aliases fragment reads from the other.
 template <int KIND>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
                                                          const bf16* __restrict__ Bt, int ldb,
                                                          int M, int N, int K, Epilogue epi) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE_BYTES];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE_BYTES];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
 
-  // global -> LDS mapping: thread owns 16-byte chunk lc of rows lr + 32 i, i < 8
-  const int lc = tid & 7, lr = tid >> 3;
-  const int voff_a = lr * lda * 2 + lc * 16, step_a = 32 * lda * 2;
-  const int voff_b = lr * ldb * 2 + lc * 16, step_b = 32 * ldb * 2;
-  const int woff = lr * 128 + ((lc ^ (lr & 7)) << 4);   // + i * 32 rows * 128 B
-
-  uint4 ra_[8], rb_[8];
-  auto gload = [&](int kt) {
-    const __amdgpu_buffer_rsrc_t sa = slab_rsrc(A, m0, rows_a, lda, kt * BK);
-    const __amdgpu_buffer_rsrc_t sb = slab_rsrc(Bt, n0, rows_b, ldb, kt * BK);
+  // DMA: wave instruction j covers rows 8 * (4 j + wave) .. +7 of each operand slab
+  // LDS row r holds its logical 16-byte chunk c at position c ^ ((r >> 1) & 7): a
+  // b128 read is served 16 lanes (rows r..r+15) per pass over 64 four-byte banks,
+  // and (row parity, (r >> 1) & 7) gives those 16 rows 16 distinct bank groups.
+  // Rows 8 (4 j + wave) + lrow have (r >> 1) & 7 = (4 (wave & 1) + (lrow >> 1)) & 7.
+  const int lrow = lane >> 3;
+  const int lchunk = (lane & 7) ^ ((4 * (wave & 1) + (lrow >> 1)) & 7);
+  const int voff_a = (8 * wave + lrow) * lda * 2 + lchunk * 16, step_a = 32 * lda * 2;
+  const int voff_b = (8 * wave + lrow) * ldb * 2 + lchunk * 16, step_b = 32 * ldb * 2;
+  const int ldsw = wave * 1024;
+  auto dma = [&](uint8_t* stage, int kt) {
+    const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, rows_a, lda, kt * BK);
+    const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, rows_b, ldb, kt * BK);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      auto va = __builtin_amdgcn_raw_buffer_load_b128(sa, voff_a + i * step_a, 0, 0);
-      auto vb = __builtin_amdgcn_raw_buffer_load_b128(sb, voff_b + i * step_b, 0, 0);
-      ra_[i] = *reinterpret_cast<uint4*>(&va);
-      rb_[i] = *reinterpret_cast<uint4*>(&vb);
-    }
-  };
-  auto lstore = [&](int stage) {
-    uint8_t* sa = smem + stage * STAGE_BYTES;
-    uint8_t* sb = sa + TILE_BYTES;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      *reinterpret_cast<uint4*>(sa + woff + i * 32 * 128) = ra_[i];
-      *reinterpret_cast<uint4*>(sb + woff + i * 32 * 128) = rb_[i];
+    for (int j = 0; j < 8; ++j) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + ldsw + j * 4096), 16,
+                                               voff_a + j * step_a, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + TILE_BYTES + ldsw + j * 4096),
+                                               16, voff_b + j * step_b, 0, 0, 0);
     }
   };
 
-  // fragment mapping: lane reads row (l % 32) of a 32-row tile, k half (l / 32)
+  // fragments: lane reads row (l % 32) of a 32-row MFMA tile, k half (l / 32)
   const int wm = wave >> 1, wn = wave & 1;
   const int fr = lane & 31, fk = lane >> 5;
   const int arow = (wm * 128 + fr) * 128;
-  const int brow = (wn * 128 + fr) * 128;
+  const int brow = TILE_BYTES + (wn * 128 + fr) * 128;
 
   f32x16_t acc[4][4];
 #pragma unroll
@@ -175,35 +181,56 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int KT = K / BK;
-  for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload(kt + 1);
-    const uint8_t* sa = smem + (kt & 1) * STAGE_BYTES;
-    const uint8_t* sb = sa + TILE_BYTES;
+  bf16x8_t fa[2][4], fb[2][4];
+  auto frags = [&](const uint8_t* stage, int s, int buf) {
+    const int pc = ((2 * s + fk) ^ ((fr >> 1) & 7)) << 4;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int pc = ((2 * s + fk) ^ (fr & 7)) << 4;
-      bf16x8_t a[4], b[4];
+    for (int i = 0; i < 4; ++i)
+      fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(stage + arow + i * 4096 + pc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(sa + arow + i * 32 * 128 + pc);
+    for (int j = 0; j < 4; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(stage + brow + j * 4096 + pc);
+  };
+  // The weight tile is the MFMA's first operand, so D[i][j] has j = output row
+  // (lane % 32) and i = output column 8 (r / 4) + 4 (lane / 32) + r % 4.
+  auto mfma = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(sb + brow + j * 32 * 128 + pc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[j], a[i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  const int KT = K / BK;
+  // One K-slab from `cur`.  Fragments of the next substep are read while this
+  // substep's 16 MFMAs run (sched_barrier keeps the order).  Before the last
+  // substep's MFMAs the block waits for the next slab's DMA, syncs, starts the
+  // slab after next into `cur` and reads the next slab's first fragments.
+#define CEM_FENCE __builtin_amdgcn_sched_barrier(0)
+  auto slab = [&](uint8_t* cur, uint8_t* nxt, int kt) {
+    frags(cur, 1, 1); CEM_FENCE; mfma(0); CEM_FENCE;
+    frags(cur, 2, 0); CEM_FENCE; mfma(1); CEM_FENCE;
+    frags(cur, 3, 1); CEM_FENCE; mfma(0); CEM_FENCE;
+    if (kt + 1 < KT) {
+      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
+      __syncthreads();
+      if (kt + 2 < KT) dma(cur, kt + 2);
+      frags(nxt, 0, 0);
     }
-    if (kt + 1 < KT) lstore((kt + 1) & 1);
-    __syncthreads();
+    CEM_FENCE; mfma(1); CEM_FENCE;
+  };
+  dma(st0, 0);
+  __builtin_amdgcn_s_waitcnt(0x0070);
+  __syncthreads();
+  if (KT > 1) dma(st1, 1);
+  frags(st0, 0, 0);
+  int kt = 0;
+  for (; kt + 1 < KT; kt += 2) {
+    slab(st0, st1, kt);
+    slab(st1, st0, kt + 1);
   }
+  if (kt < KT) slab(st0, st1, kt);
+#undef CEM_FENCE
 
-  // D[i][j] of one MFMA: j = lane % 32 (output row), i = 8 (r / 4) + 4 (lane / 32) + r % 4
   const int ncol = n0 + wn * 128 + 4 * fk;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {

@@ -100,8 +100,11 @@ def test_energy_l1_matches_oracle(gpu_lib, dtype, n, p, e):
     if dtype == "bf16":
         tz = tz.to(torch.bfloat16)
     out = torch.full((max(n, 1),), -1.0, dtype=torch.float32, device="cuda")
-    _lib.load().energy_l1(tz.data_ptr(), 1 if dtype == "bf16" else 0, to_dev(zg).data_ptr(), n, p, e,
-                          out.data_ptr(), None)
+    if n == 0:
+        _lib.load().energy_l1(tz.data_ptr(), 1 if dtype == "bf16" else 0, to_dev(zg).data_ptr(), 0, p, e,
+                              out.data_ptr(), None)
+    else:
+        _lib.energy_l1(tz.reshape(n, p, e), to_dev(zg), out)
     torch.cuda.synchronize()
     if n == 0:
         assert to_np(out)[0] == -1.0
@@ -154,5 +157,16 @@ def test_energy_l1_device_generated_inputs(gpu_lib):
     torch.cuda.synchronize()
     got, want = to_np(out), to_np(ref)
     log(f"  ours: nan {int(np.isnan(got).sum())}, untouched {int((got == -7.0).sum())}; "
-        f"torch: nan {int(np.isnan(want).sum())}; inputs finite {bool(torch.isfinite(zp).all())}")
+        f"torch: nan {int(np.isnan(want).sum())}; inputs finite {bool(torch.isfinite(zp).all())} "
+        f"{bool(torch.isfinite(zg).all())}; ptrs {zp.data_ptr():#x} {zg.data_ptr():#x} {out.data_ptr():#x}")
+    out2 = torch.full((800,), -7.0, dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    _lib.energy_l1(zp, zg, out2)
+    torch.cuda.synchronize()
+    again = to_np(out2)
+    zero = torch.zeros_like(zg)
+    out3 = torch.empty(800, dtype=torch.float32, device="cuda")
+    _lib.energy_l1(zp, zero, out3)
+    torch.cuda.synchronize()
+    log(f"  recompute after sync: nan {int(np.isnan(again).sum())}; goal 0: nan {int(np.isnan(to_np(out3)).sum())}")
     np.testing.assert_allclose(got, want, rtol=2e-5, atol=0)
