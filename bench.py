@@ -30,6 +30,88 @@ sys.path.insert(0, ROOT)
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (reference for fp32 models)
 
+# HBM-side bytes per dense-GEMM launch, from two rocprofv3 --pmc passes over
+# `bench.py --steps 1 --warmup 0 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE,
+# KiB per dispatch, launch-weighted mean over every gemm_bf16_kernel dispatch),
+# each scaled by what the same counter reads for a 1 GiB device copy
+# (`bench.py --copy-bytes 1073741824`): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
+# Valid only for the GEMM sources they were taken on (sha256 below); reported
+# as null once those change.
+GEMM_COUNTERS = {
+    "sources_sha256": "8f2db56b3fe39ecdc6b7ac168c7ce013e527c7747cf71586298c9d35b3e9c25a",
+    "bytes_per_launch": 4236798648,
+}
+GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
+
+
+def gemm_sources_sha256() -> str:
+    import hashlib
+
+    h = hashlib.sha256()
+    for rel in GEMM_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def summarize_stats(path: str, top: int = 12) -> None:
+    """Markdown table of a rocprofv3 --stats kernel_stats.csv, plus the
+    launch-weighted mean duration of the dense-GEMM kernel (all epilogue kinds)."""
+    import csv
+
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    total = sum(float(r["TotalDurationNs"]) for r in rows)
+    print("| kernel | calls | avg (us) | total (ms) | share |")
+    print("|---|---:|---:|---:|---:|")
+    for r in rows[:top]:
+        name = r["Name"].replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        print(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+              f"{float(r['TotalDurationNs']) / 1e6:.1f} | {float(r['TotalDurationNs']) / total:.1%} |")
+    g = [r for r in rows if "gemm_bf16_kernel" in r["Name"]]
+    calls = sum(int(r["Calls"]) for r in g)
+    ns = sum(float(r["TotalDurationNs"]) for r in g)
+    if calls:
+        print(f"\ngemm_bf16_kernel, all kinds: {calls} launches, mean {ns / calls / 1e6:.4f} ms per launch")
+
+
+def summarize_traffic(fetch: str, write: str, copy_fetch: str, copy_write: str,
+                      copy_bytes: int) -> None:
+    """Per-kernel FETCH_SIZE / WRITE_SIZE means (KiB per dispatch) of two
+    rocprofv3 --pmc passes, scaled by the copy calibration."""
+    import collections
+    import csv
+
+    def per_kernel(path):
+        d = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            d[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return d
+
+    def copy_mean(path):
+        d = per_kernel(path)
+        v = [x for k, xs in d.items() if "copyBuffer" in k or "copy" in k.lower() for x in xs]
+        return sum(v) / len(v)
+
+    kib = copy_bytes / 1024
+    ff, fw = kib / copy_mean(copy_fetch), kib / copy_mean(copy_write)
+    print(f"copy calibration ({copy_bytes} bytes): FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}\n")
+    df, dw = per_kernel(fetch), per_kernel(write)
+    print("| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes / dispatch |")
+    print("|---|---:|---:|---:|---:|")
+    keys = sorted(df, key=lambda k: -sum(df[k]))
+    for k in keys[:10]:
+        f = sum(df[k]) / len(df[k])
+        w = sum(dw.get(k, [0.0])) / max(len(dw.get(k, [])), 1)
+        name = k.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+        print(f"| `{name}` | {len(df[k])} | {f:.1f} | {w:.1f} | {(f * ff + w * fw) * 1024:.4g} |")
+    gf = [x for k, xs in df.items() if "gemm_bf16_kernel" in k for x in xs]
+    gw = [x for k, xs in dw.items() if "gemm_bf16_kernel" in k for x in xs]
+    if gf and gw:
+        b = (sum(gf) / len(gf) * ff + sum(gw) / len(gw) * fw) * 1024
+        print(f"\ngemm_bf16_kernel, all kinds: {len(gf)} dispatches, {b:.0f} bytes per launch; "
+              f"GEMM sources sha256 {gemm_sources_sha256()}")
+
 
 def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -97,7 +179,19 @@ def main() -> int:
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration only: run a plain device copy of this many bytes 3 times "
                          "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
+                    help="print a markdown summary of a rocprofv3 --stats CSV and exit")
+    ap.add_argument("--summarize-traffic", nargs=4,
+                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="print per-kernel HBM bytes from rocprofv3 --pmc CSVs (FETCH_SIZE, "
+                         "WRITE_SIZE of the bench; the same of the --copy-bytes run) and exit")
     args = ap.parse_args()
+    if args.summarize_stats:
+        summarize_stats(args.summarize_stats)
+        return 0
+    if args.summarize_traffic:
+        summarize_traffic(*args.summarize_traffic, copy_bytes=args.copy_bytes or (1 << 30))
+        return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -190,8 +284,13 @@ def main() -> int:
         model.timer_enable(False)
         peak = MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
         achieved = flop / (gemm_ms * 1e-3) / 1e12
+        traffic = None
+        if m.dtype == "bf16" and gemm_sources_sha256() == GEMM_COUNTERS["sources_sha256"]:
+            traffic = GEMM_COUNTERS["bytes_per_launch"]
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4), "traffic": None,
+                "frac": round(achieved / peak, 4), "traffic": traffic,
+                "traffic_unit": "HBM-side bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
+                                "copy-calibrated)",
                 "kernel": "gemm_bf16_kernel" if m.dtype == "bf16" else "gemm_f32_kernel",
                 "launches": launches, "avg_launch_ms": round(gemm_ms / max(launches, 1), 4),
                 "gemm_share_of_step": round(gemm_ms / args.steps / eager_ms, 4)}

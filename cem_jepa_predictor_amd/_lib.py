@@ -62,7 +62,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with `python -m cem_jepa_predictor_amd.build`")
+    # torch ships its own HIP runtime; importing it first makes the library bind to
+    # that same runtime (same SONAME), so both share one device context and streams.
+    import torch  # noqa: F401
+
     lib = ctypes.CDLL(path)
+    runtimes = _hip_runtimes_mapped()
+    if len(runtimes) > 1:
+        raise RuntimeError("two HIP runtimes are mapped in this process (" + ", ".join(runtimes)
+                           + "): import torch before anything that loads libamdhip64")
     lib.cem_last_error.restype = ctypes.c_char_p
     lib.cem_last_error.argtypes = []
     sigs = {
@@ -88,15 +96,62 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return lib
 
 
+def _hip_runtimes_mapped():
+    """Distinct libamdhip64 files mapped into this process (Linux /proc)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64.so" in line}
+    except OSError:
+        return []
+    return sorted({os.path.realpath(p) for p in paths})
+
+
 def _check(status: int) -> None:
     if status != 0:
         raise CemError(status, load().cem_last_error().decode())
 
 
-def _ptr(t) -> Optional[int]:
-    if t is None:
-        return None
-    return t.data_ptr()
+def _args(*specs):
+    """Device pointers of tensor arguments after checking what the C ABI assumes of
+    them; raises before any library call.  Each spec is (tensor, name, dtypes[, shape
+    [, optional]]).  dtype and shape of every argument are checked before device
+    residency and contiguity, so a wrong dtype is reported as such even for host
+    tensors."""
+    import torch
+
+    full = [tuple(sp) + (None, False)[len(sp) - 3:] for sp in specs]
+    for t, name, dtypes, shape, optional in full:
+        if t is None:
+            if optional:
+                continue
+            raise ValueError(f"{name} is required")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if t.dtype not in dtypes:
+            raise TypeError(f"{name}: dtype {t.dtype}, expected {' or '.join(str(d) for d in dtypes)}")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+    ptrs = []
+    for t, name, _, _, _ in full:
+        if t is None:
+            ptrs.append(None)
+            continue
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device (cuda) tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        ptrs.append(t.data_ptr())
+    return ptrs
+
+
+def _f32():
+    import torch
+    return (torch.float32,)
+
+
+def _i32():
+    import torch
+    return (torch.int32,)
 
 
 _side_streams = {}
@@ -177,24 +232,40 @@ class Model:
     def plan(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
              n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,
              clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True, stream=None):
+        c = self.cfg
+        pe, ha = (c.patches, c.enc_dim), (horizon, c.action_dim)
+        ptrs = _args((z_obs, "z_obs", _f32(), pe), (z_goal, "z_goal", _f32(), pe),
+                     (s0, "s0", _f32(), (c.state_dim,)), (mu, "mu", _f32(), ha),
+                     (sigma, "sigma", _f32(), ha), (action, "action", _f32(), (c.action_dim,)),
+                     (best_idx, "best_idx", _i32(), (1,), True))
         p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
                    1 if use_graph else 0)
         with _OnStream(stream) as st:
-            _check(load().cem_plan(self.handle, ctypes.byref(p), _ptr(z_obs), _ptr(z_goal), _ptr(s0),
-                                   _ptr(mu), _ptr(sigma), _ptr(action), _ptr(best_idx), st))
+            _check(load().cem_plan(self.handle, ctypes.byref(p), *ptrs, st))
         self._last = p
 
     def trace(self, kind: int, out, stream=None):
+        """Copies one per-round record of the last plan into `out` (int32 for the
+        elite indices, float32 otherwise; the library checks the byte size)."""
+        ptr, = _args((out, "out", _i32() if kind == TRACE_ELITES else _f32()))
         with _OnStream(stream) as st:
-            _check(load().cem_plan_trace(self.handle, kind, _ptr(out), out.numel() * out.element_size(),
-                                         st))
+            _check(load().cem_plan_trace(self.handle, kind, ptr, out.numel() * out.element_size(), st))
         return out
 
     def rollout(self, actions, z_obs, s0, z_pred, stream=None):
+        import torch
+
+        c = self.cfg
+        if actions.dim() != 3:
+            raise ValueError(f"actions: expected [n, h, {c.action_dim}], got {tuple(actions.shape)}")
         n, h = actions.shape[0], actions.shape[1]
+        zdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        ptrs = _args((actions, "actions", _f32(), (n, h, c.action_dim)),
+                     (z_obs, "z_obs", _f32(), (c.patches, c.enc_dim)),
+                     (s0, "s0", _f32(), (c.state_dim,)),
+                     (z_pred, "z_pred", (zdt,), (n, c.patches, c.enc_dim)))
         with _OnStream(stream) as st:
-            _check(load().predictor_rollout(self.handle, _ptr(actions), n, h, _ptr(z_obs), _ptr(s0),
-                                            _ptr(z_pred), st))
+            _check(load().predictor_rollout(self.handle, ptrs[0], n, h, ptrs[1], ptrs[2], ptrs[3], st))
         return z_pred
 
     def timer_enable(self, on: bool = True):
@@ -209,27 +280,50 @@ class Model:
 def energy_l1(z_pred, z_goal, energy, stream=None):
     import torch
 
-    dt = CEM_BF16 if z_pred.dtype == torch.bfloat16 else CEM_F32
+    if z_pred.dim() != 3:
+        raise ValueError(f"z_pred: expected [n, p, e], got {tuple(z_pred.shape)}")
     n, p, e = z_pred.shape
+    zp, zg, en = _args((z_pred, "z_pred", (torch.bfloat16, torch.float32)),
+                       (z_goal, "z_goal", _f32(), (p, e)), (energy, "energy", _f32(), (n,)))
+    dt = CEM_BF16 if z_pred.dtype == torch.bfloat16 else CEM_F32
     with _OnStream(stream) as st:
-        _check(load().energy_l1(_ptr(z_pred), dt, _ptr(z_goal), n, p, e, _ptr(energy), st))
+        _check(load().energy_l1(zp, dt, zg, n, p, e, en, st))
     return energy
 
 
 def elite_refit(energy, actions, k, elite_idx, mu, sigma, stream=None):
+    if actions.dim() != 3:
+        raise ValueError(f"actions: expected [n, h, a], got {tuple(actions.shape)}")
     n, h, a = actions.shape
+    ptrs = _args((energy, "energy", _f32(), (n,)), (actions, "actions", _f32()),
+                 (elite_idx, "elite_idx", _i32(), (k,)), (mu, "mu", _f32(), (h, a)),
+                 (sigma, "sigma", _f32(), (h, a)))
     with _OnStream(stream) as st:
-        _check(load().elite_refit(_ptr(energy), _ptr(actions), n, k, h, a, _ptr(elite_idx), _ptr(mu),
-                                  _ptr(sigma), st))
+        _check(load().elite_refit(ptrs[0], ptrs[1], n, k, h, a, ptrs[2], ptrs[3], ptrs[4], st))
 
 
 def cem_sample(mu, sigma, n, seed, rnd, plan_id, lo, hi, actions, raw_words=None, stream=None):
+    import torch
+
+    if mu.dim() != 2:
+        raise ValueError(f"mu: expected [h, a], got {tuple(mu.shape)}")
     h, a = mu.shape
+    if actions.dim() != 3 or tuple(actions.shape[1:]) != (h, a) or actions.shape[0] < n:
+        raise ValueError(f"actions: shape {tuple(actions.shape)}, expected [>= {n}, {h}, {a}]")
+    if raw_words is not None and raw_words.numel() < n * h * a:
+        raise ValueError(f"raw_words: {raw_words.numel()} elements, need {n * h * a}")
+    mp, sp, xp, raw = _args((mu, "mu", _f32()), (sigma, "sigma", _f32(), (h, a)),
+                            (actions, "actions", _f32()),
+                            (raw_words, "raw_words", (torch.int32, torch.uint32), None, True))
+    ptrs = (mp, sp, xp)
     with _OnStream(stream) as st:
-        _check(load().cem_sample(_ptr(mu), _ptr(sigma), n, h, a, seed, rnd, plan_id, lo, hi,
-                                 _ptr(actions), _ptr(raw_words), st))
+        _check(load().cem_sample(ptrs[0], ptrs[1], n, h, a, seed, rnd, plan_id, lo, hi, ptrs[2], raw,
+                                 st))
 
 
 def topk_select(energy, k, idx, stream=None):
+    if energy.dim() != 1:
+        raise ValueError(f"energy: expected 1-d, got {tuple(energy.shape)}")
+    ptrs = _args((energy, "energy", _f32()), (idx, "idx", _i32(), (k,)))
     with _OnStream(stream) as st:
-        _check(load().topk_select(_ptr(energy), energy.numel(), k, _ptr(idx), st))
+        _check(load().topk_select(ptrs[0], energy.numel(), k, ptrs[1], st))

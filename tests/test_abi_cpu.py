@@ -110,3 +110,22 @@ def test_plan_calls_validate_null_model(lib):
     assert lib.predictor_rollout(None, fake, 1, 1, fake, fake, fake, None) == -1
     assert lib.cem_plan_trace(None, 0, fake, 4, None) == -1
     assert lib.cem_timer_enable(None, 1) == -1
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    """dtype, shape, device and layout are checked in the binding, before any pointer
+    crosses the ABI (a float64 goal read as float32 would give garbage energies)."""
+    import torch
+
+    zp = torch.zeros((2, 3, 8), dtype=torch.bfloat16)
+    out = torch.zeros(2, dtype=torch.float32)
+    with pytest.raises(TypeError, match="z_goal: dtype torch.float64"):
+        _lib.energy_l1(zp, torch.zeros((3, 8), dtype=torch.float64), out)
+    with pytest.raises(ValueError, match=r"z_goal: shape \(8, 3\)"):
+        _lib.energy_l1(zp, torch.zeros((8, 3), dtype=torch.float32), out)
+    with pytest.raises(ValueError, match="must be a device"):
+        _lib.energy_l1(zp, torch.zeros((3, 8), dtype=torch.float32), out)
+    with pytest.raises(TypeError, match="idx: dtype torch.int64"):
+        _lib.topk_select(torch.zeros(4), 2, torch.zeros(2, dtype=torch.int64))
+    with pytest.raises(TypeError, match="out: dtype torch.float32"):
+        _lib.Model.trace(None, _lib.TRACE_ELITES, torch.zeros(4))

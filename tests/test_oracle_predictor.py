@@ -6,7 +6,16 @@ import torch
 from cem_jepa_predictor_amd import inputs
 from oracle import predictor as P
 
-torch.set_default_dtype(torch.float64)
+
+
+@pytest.fixture(autouse=True, scope="module")
+def _float64_modules():
+    """torch.nn modules built here get float64 parameters; the global default is
+    restored afterwards so other test modules keep float32."""
+    prev = torch.get_default_dtype()
+    torch.set_default_dtype(torch.float64)
+    yield
+    torch.set_default_dtype(prev)
 
 
 def _t(x):
