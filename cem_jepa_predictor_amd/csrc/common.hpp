@@ -74,20 +74,25 @@ __device__ __forceinline__ float gelu_exact(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));
 }
 
-// GELU(x) = x * Phi(x) for bf16 models, branch-free.  Phi(-|x|) = erfc(z) / 2 with
-// z = |x| / sqrt(2) and erfc(z) ~= t (a1 + a2 t + ... + a5 t^4) exp(-z^2),
-// t = 1 / (1 + p z): Abramowitz & Stegun, Handbook of Mathematical Functions,
-// eq. 7.1.26 (Hastings), |erf error| <= 1.5e-7 -- four orders of magnitude
-// below the bf16 rounding applied to the result.
+// GELU(x) = x * Phi(x) for bf16 models, branch-free.  With h = Phi(-|x|):
+// GELU(x) = max(x, 0) - |x| h for either sign.  h = erfc(z) / 2, z = |x| / sqrt(2),
+// erfc(z) ~= t (a1 + a2 t + ... + a5 t^4) exp(-z^2), t = 1 / (1 + p z):
+// Abramowitz & Stegun, Handbook of Mathematical Functions, eq. 7.1.26
+// (Hastings), |erf error| <= 1.5e-7 -- four orders of magnitude below the bf16
+// rounding applied to the result.  The 1/2, the 1/sqrt(2) and log2(e) are folded
+// into the constants; exp(-z^2) = 2^(-x^2 log2(e) / 2) goes straight to the
+// hardware exp2, whose flush of tiny results only drops terms far below the
+// bf16 resolution of x.
 __device__ __forceinline__ float gelu_bf16_path(float x) {
-  const float z = fabsf(x) * 0.70710678118654752440f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, z, 1.0f));
-  float poly = fmaf(t, 1.061405429f, -1.453152027f);
-  poly = fmaf(t, poly, 1.421413741f);
-  poly = fmaf(t, poly, -0.284496736f);
-  poly = fmaf(t, poly, 0.254829592f);
-  const float h = 0.5f * t * poly * __expf(-z * z);   // Phi(-|x|)
-  return x * (x >= 0.f ? 1.0f - h : h);
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(ax, 0.3275911f * 0.70710678118654752f, 1.0f));
+  float poly = fmaf(t, 0.5f * 1.061405429f, 0.5f * -1.453152027f);
+  poly = fmaf(t, poly, 0.5f * 1.421413741f);
+  poly = fmaf(t, poly, 0.5f * -0.284496736f);
+  poly = fmaf(t, poly, 0.5f * 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);
+  const float h = (poly * t) * e;
+  return fmaf(-ax, h, fmaxf(x, 0.f));
 }
 
 }  // namespace cem

@@ -13,21 +13,19 @@
 //    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
 //  * The MFMA's first operand is the weight tile and its second the
 //    activation tile, so each lane's accumulator quads hold 4 consecutive
-//    output columns of one output row: the epilogue reads bias / residual and
-//    writes 8-byte (bf16) vectors.
-//  * LDS double buffer (2 x 64 KB) filled by LDS-DMA buffer loads (global ->
-//    LDS without VGPRs), the slab after next in flight during the current
-//    slab's MFMAs; fragments double-buffered in registers so each substep's
-//    LDS reads overlap the previous substep's MFMAs; one barrier per slab,
-//    placed before the last substep's MFMAs.  Rows of 64 bf16 (128 B) are
-//    stored as eight 16-byte chunks, chunk c of row r at position
-//    c ^ ((r >> 1) & 7), so fragment reads are free of bank conflicts.
+//    output columns of one output row.
+//  * Operands: global -> VGPR (buffer_load_dwordx4, two staging register sets)
+//    -> LDS double buffer (2 x 64 KB), memory two slabs ahead of the MFMAs,
+//    every memory instruction placed between MFMAs (see the main loop).
+//    128-byte LDS rows hold their eight 16-byte chunks at c ^ ((r >> 1) & 7),
+//    so fragment reads are free of bank conflicts.
 //  * Block -> tile map is XCD-aware: the dispatcher hands block b to XCD
 //    b % 8, so each XCD receives a contiguous range of logical tiles, ordered
 //    in groups of 8 row-tiles to share A and B panels in that XCD's L2.
 //  * Ragged M / N: operand loads go through buffer resources bounded at the
 //    tile's last valid row (the hardware returns zero beyond it), stores are
 //    masked.
+//  * Results leave through LDS as full rows (see the epilogue).
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
 //    each carries only its own epilogue code.
 //
@@ -125,12 +123,26 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, in
       const_cast<bf16*>(base + (long long)row0 * ld + k), (short)0, (int)bytes, 0x00020000);
 }
 
-// Operand slabs go global -> LDS directly (buffer_load ... lds, 16 bytes per
-// lane at m0 + 16 * lane), so the data never occupies VGPRs.  Each wave
-// instruction fills 8 rows of 128 bytes; lane l loads row r = base + l / 8 and
-// the logical 16-byte chunk that belongs at LDS position l % 8 under the
-// swizzle.  Two stage arrays (distinct objects) let the compiler
-// see that DMA into one stage never aliases fragment reads from the other.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Main loop.  Operand slabs (BK = 64 columns of 256 A rows and 256 B rows,
+// 128 contiguous bytes per row) go global -> VGPR -> LDS through two staging
+// register sets, so memory runs two slabs ahead of the MFMAs without a third
+// LDS stage: during slab kt the wave issues slab kt+2's loads (4 per substep)
+// and writes slab kt+1 (loaded during slab kt-1) into the free LDS stage
+// (substeps 0-2), each interleaved one per MFMA so no burst of memory
+// instructions holds up MFMA issue.  One barrier per slab, before the last
+// substep's MFMAs; it waits for LDS traffic only.  Loads of slabs at or past K
+// use an empty buffer resource (zeros, no memory traffic), which keeps every
+// slab of the loop identical; an odd slab count runs one extra all-zero slab.
+//
+// Epilogue.  When a tile maps to one destination with 16-byte aligned rows,
+// each wave stages its 128 x 128 result in 32 KB of the freed operand LDS and
+// then writes full rows (16 bytes a lane, 4 rows x 256 bytes per
+// instruction) instead of 16-byte pieces of 32 rows.  Plain / GELU values are
+// staged as bf16 (rounded once, as before); the residual kind stages fp32 in
+// two 64-row halves and adds the residual rows, loaded first, in fp32, so it
+// also rounds once.  Other tiles take the per-4-column path.
 template <int KIND>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
                                                          const bf16* __restrict__ Bt, int ldb,
@@ -145,26 +157,35 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
 
-  // DMA: wave instruction j covers rows 8 * (4 j + wave) .. +7 of each operand slab
-  // LDS row r holds its logical 16-byte chunk c at position c ^ ((r >> 1) & 7): a
-  // b128 read is served 16 lanes (rows r..r+15) per pass over 64 four-byte banks,
-  // and (row parity, (r >> 1) & 7) gives those 16 rows 16 distinct bank groups.
-  // Rows 8 (4 j + wave) + lrow have (r >> 1) & 7 = (4 (wave & 1) + (lrow >> 1)) & 7.
-  const int lrow = lane >> 3;
-  const int lchunk = (lane & 7) ^ ((4 * (wave & 1) + (lrow >> 1)) & 7);
-  const int voff_a = (8 * wave + lrow) * lda * 2 + lchunk * 16, step_a = 32 * lda * 2;
-  const int voff_b = (8 * wave + lrow) * ldb * 2 + lchunk * 16, step_b = 32 * ldb * 2;
-  const int ldsw = wave * 1024;
-  auto dma = [&](uint8_t* stage, int kt) {
-    const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, rows_a, lda, kt * BK);
-    const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, rows_b, ldb, kt * BK);
+  // Global loads: wave instruction j covers rows 8 (4 j + wave) .. +7 of an operand
+  // slab, lane l row + l / 8, logical 16-byte chunk l % 8.  LDS row r holds its
+  // logical chunk c at position c ^ ((r >> 1) & 7): a b128 fragment read is served
+  // 16 lanes (rows r..r+15) per pass over 64 four-byte banks, and (row parity,
+  // (r >> 1) & 7) gives those 16 rows 16 distinct bank groups.  Rows
+  // 8 (4 j + wave) + lrow have (r >> 1) & 7 = (4 (wave & 1) + (lrow >> 1)) & 7.
+  const int lrow = lane >> 3, lc = lane & 7;
+  const int sw = (4 * (wave & 1) + (lrow >> 1)) & 7;
+  const int goff_a = (8 * wave + lrow) * lda * 2 + lc * 16, gstep_a = 32 * lda * 2;
+  const int goff_b = (8 * wave + lrow) * ldb * 2 + lc * 16, gstep_b = 32 * ldb * 2;
+  const int lds_w = (8 * wave + lrow) * 128 + ((lc ^ sw) << 4);
+  const int KT = K / BK;
+  // part p < 8: A rows of instruction p; p >= 8: B rows of instruction p - 8.
+  // The row offset stays in the range-checked VGPR offset (soffset is not checked).
+  auto gload = [&](u32x4* g, int kt, int p0, int p1) {
+    const bool live = kt < KT;
+    const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, live ? rows_a : 0, lda, live ? kt * BK : 0);
+    const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, live ? rows_b : 0, ldb, live ? kt * BK : 0);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(stage + ldsw + j * 4096), 16,
-                                               voff_a + j * step_a, 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(stage + TILE_BYTES + ldsw + j * 4096),
-                                               16, voff_b + j * step_b, 0, 0, 0);
+    for (int p = p0; p < p1; ++p) {
+      const int j = p & 7;
+      g[p] = (p < 8) ? __builtin_amdgcn_raw_buffer_load_b128(ra, goff_a + j * gstep_a, 0, 0)
+                     : __builtin_amdgcn_raw_buffer_load_b128(rb, goff_b + j * gstep_b, 0, 0);
     }
+  };
+  auto lstore = [&](const u32x4* g, uint8_t* stage, int p0, int p1) {
+#pragma unroll
+    for (int p = p0; p < p1; ++p)
+      *reinterpret_cast<u32x4*>(stage + (p < 8 ? 0 : TILE_BYTES) + lds_w + (p & 7) * 4096) = g[p];
   };
 
   // fragments: lane reads row (l % 32) of a 32-row MFMA tile, k half (l / 32)
@@ -172,7 +193,6 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int fr = lane & 31, fk = lane >> 5;
   const int arow = (wm * 128 + fr) * 128;
   const int brow = TILE_BYTES + (wn * 128 + fr) * 128;
-
   f32x16_t acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -180,7 +200,6 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-
   bf16x8_t fa[2][4], fb[2][4];
   auto frags = [&](const uint8_t* stage, int s, int buf) {
     const int pc = ((2 * s + fk) ^ ((fr >> 1) & 7)) << 4;
@@ -200,38 +219,165 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       for (int j = 0; j < 4; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
   };
-  const int KT = K / BK;
-  // One K-slab from `cur`.  Fragments of the next substep are read while this
-  // substep's 16 MFMAs run (sched_barrier keeps the order).  Before the last
-  // substep's MFMAs the block waits for the next slab's DMA, syncs, starts the
-  // slab after next into `cur` and reads the next slab's first fragments.
-#define CEM_FENCE __builtin_amdgcn_sched_barrier(0)
-  auto slab = [&](uint8_t* cur, uint8_t* nxt, int kt) {
-    frags(cur, 1, 1); CEM_FENCE; mfma(0); CEM_FENCE;
-    frags(cur, 2, 0); CEM_FENCE; mfma(1); CEM_FENCE;
-    frags(cur, 3, 1); CEM_FENCE; mfma(0); CEM_FENCE;
-    if (kt + 1 < KT) {
-      __builtin_amdgcn_s_waitcnt(0x0070);   // vmcnt(0) lgkmcnt(0)
-      __syncthreads();
-      if (kt + 2 < KT) dma(cur, kt + 2);
-      frags(nxt, 0, 0);
-    }
-    CEM_FENCE; mfma(1); CEM_FENCE;
+  auto lds_barrier = [&]() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); global loads stay in flight
+    __builtin_amdgcn_s_barrier();
   };
-  dma(st0, 0);
-  __builtin_amdgcn_s_waitcnt(0x0070);
-  __syncthreads();
-  if (KT > 1) dma(st1, 1);
+  // schedule of one substep: its 8 fragment reads first, then one LDS write and one
+  // global load after each of the first nw / nl MFMAs
+  auto interleave = [&](int nw, int nl) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    for (int r = 0; r < 16; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (r < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+      if (r < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+  };
+#define CEM_FENCE __builtin_amdgcn_sched_barrier(0)
+  // One K-slab from `cur`: gw holds slab kt+1 (written to `nxt`), gl receives slab kt+2.
+  auto slab = [&](uint8_t* cur, uint8_t* nxt, u32x4* gw, u32x4* gl, int kt) {
+    frags(cur, 1, 1); lstore(gw, nxt, 0, 6); gload(gl, kt + 2, 0, 4); mfma(0); interleave(6, 4);
+    CEM_FENCE;
+    frags(cur, 2, 0); lstore(gw, nxt, 6, 11); gload(gl, kt + 2, 4, 8); mfma(1); interleave(5, 4);
+    CEM_FENCE;
+    frags(cur, 3, 1); lstore(gw, nxt, 11, 16); gload(gl, kt + 2, 8, 12); mfma(0); interleave(5, 4);
+    CEM_FENCE;
+    lds_barrier();
+    frags(nxt, 0, 0); gload(gl, kt + 2, 12, 16); mfma(1); interleave(0, 4);
+    CEM_FENCE;
+  };
+  u32x4 g0[16], g1[16];
+  gload(g0, 0, 0, 16);
+  CEM_FENCE;
+  lstore(g0, st0, 0, 16);
+  CEM_FENCE;
+  gload(g1, 1, 0, 16);
+  CEM_FENCE;
+  lds_barrier();
   frags(st0, 0, 0);
-  int kt = 0;
-  for (; kt + 1 < KT; kt += 2) {
-    slab(st0, st1, kt);
-    slab(st1, st0, kt + 1);
+  CEM_FENCE;
+  for (int kt = 0; kt < KT; kt += 2) {
+    slab(st0, st1, g1, g0, kt);       // slab kt+1 from g1 into st1; slab kt+2 loads into g0
+    slab(st1, st0, g0, g1, kt + 1);
   }
-  if (kt < KT) slab(st0, st1, kt);
+  __builtin_amdgcn_s_waitcnt(0x0070);   // no load outlives the main loop
 #undef CEM_FENCE
 
   const int ncol = n0 + wn * 128 + 4 * fk;
+  const bool to_c0 = n0 + BN <= epi.split, to_c1 = n0 >= epi.split;
+  bf16* const cbase = static_cast<bf16*>(to_c0 ? epi.c0 : epi.c1);
+  const int ldc = to_c0 ? epi.ld0 : epi.ld1;
+  const int cshift = to_c0 ? 0 : epi.split;
+  if ((to_c0 || to_c1) && n0 + BN <= N && epi.bias && (ldc & 7) == 0 && (cshift & 7) == 0 &&
+      epi.rows.group >= 4 && ((uintptr_t)cbase & 15) == 0) {
+    lds_barrier();   // every wave is done with the operand stages
+    uint8_t* const ep = (wave < 2 ? st0 : st1) + (wave & 1) * 32768;
+    const float* const bias = epi.bias + ncol;
+    bf16* const cwave = cbase + (n0 + wn * 128 - cshift);
+    const int row_base = m0 + wm * 128;
+    // destination rows of one lane, advanced incrementally (row map group >= 4)
+    struct RowWalk {
+      long long quot;
+      int rem;
+    };
+    auto row_walk = [&](int r) {
+      const int m = row_base + r;
+      return RowWalk{(long long)(m / epi.rows.group), m % epi.rows.group};
+    };
+    auto row_of = [&](const RowWalk& w) { return w.quot * epi.rows.stride + epi.rows.offset + w.rem; };
+    auto row_step = [&](RowWalk& w, int d) {
+      w.rem += d;
+      if (w.rem >= epi.rows.group) { w.rem -= epi.rows.group; ++w.quot; }
+    };
+    if constexpr (KIND != kEpiResidual) {
+      // bf16 staging: row r (256 bytes) holds 16-byte chunk c at c ^ (r & 15)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = i * 32 + fr;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 bb = *reinterpret_cast<const float4*>(bias + j * 32 + 8 * q);
+            float v[4] = {acc[i][j][4 * q] + bb.x, acc[i][j][4 * q + 1] + bb.y,
+                          acc[i][j][4 * q + 2] + bb.z, acc[i][j][4 * q + 3] + bb.w};
+            if constexpr (KIND == kEpiGelu) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = gelu_bf16_path(v[e]);
+            }
+            uint2 u;
+            u.x = pack_bf16x2(v[0], v[1]);
+            u.y = pack_bf16x2(v[2], v[3]);
+            const int c16 = 4 * j + q;
+            *reinterpret_cast<uint2*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4) + fk * 8) = u;
+          }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's staging writes are done
+      const int c16 = lane & 15;
+      RowWalk w = row_walk(lane >> 4);
+#pragma unroll 4
+      for (int t = 0; t < 32; ++t) {
+        const int r = 4 * t + (lane >> 4);
+        const uint4 d = *reinterpret_cast<const uint4*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4));
+        if (row_base + r < M) *reinterpret_cast<uint4*>(cwave + row_of(w) * ldc + c16 * 8) = d;
+        row_step(w, 4);
+      }
+    } else {
+      // fp32 staging in two 64-row halves (row r: 512 bytes, 16-byte chunk c at
+      // c ^ (r & 15)); each half's residual rows are loaded first so their latency
+      // overlaps the staging writes
+      const int ch = lane & 31;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        uint2 res[32];
+        {
+          RowWalk w = row_walk(64 * h + (lane >> 5));
+#pragma unroll
+          for (int t = 0; t < 32; ++t) {
+            const int r = 64 * h + 2 * t + (lane >> 5);
+            res[t] = make_uint2(0u, 0u);
+            if (row_base + r < M)
+              res[t] = *reinterpret_cast<const uint2*>(cwave + row_of(w) * ldc + ch * 4);
+            row_step(w, 2);
+          }
+        }
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii) {
+          const int i = 2 * h + ii;
+          const int r = ii * 32 + fr;
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float4 bb = *reinterpret_cast<const float4*>(bias + j * 32 + 8 * q);
+              const float4 v = make_float4(acc[i][j][4 * q] + bb.x, acc[i][j][4 * q + 1] + bb.y,
+                                           acc[i][j][4 * q + 2] + bb.z, acc[i][j][4 * q + 3] + bb.w);
+              const int cw = 8 * j + 2 * q + fk;
+              *reinterpret_cast<float4*>(ep + r * 512 + ((cw ^ (r & 15)) << 4)) = v;
+            }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        RowWalk w = row_walk(64 * h + (lane >> 5));
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+          const int r = 2 * t + (lane >> 5);
+          const float4 f = *reinterpret_cast<const float4*>(ep + r * 512 + ((ch ^ (r & 15)) << 4));
+          if (row_base + 64 * h + r < M) {
+            const uint2 u = res[t];
+            float v[4] = {__uint_as_float(u.x << 16) + f.x, __uint_as_float(u.x & 0xffff0000u) + f.y,
+                          __uint_as_float(u.y << 16) + f.z, __uint_as_float(u.y & 0xffff0000u) + f.w};
+            Store4<bf16>::store(cwave + row_of(w) * ldc + ch * 4, v);
+          }
+          row_step(w, 2);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);   // this half's reads are done before the next overwrites it
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm * 128 + i * 32 + fr;
