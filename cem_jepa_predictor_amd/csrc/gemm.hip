@@ -246,12 +246,12 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     frags(nxt, 0, 0); gload(gl, kt + 2, 12, 16); mfma(1); interleave(0, 4);
     CEM_FENCE;
   };
+  // prologue: slabs 0 and 1 in flight together; slab 0 goes to LDS as it lands
   u32x4 g0[16], g1[16];
   gload(g0, 0, 0, 16);
+  gload(g1, 1, 0, 16);
   CEM_FENCE;
   lstore(g0, st0, 0, 16);
-  CEM_FENCE;
-  gload(g1, 1, 0, 16);
   CEM_FENCE;
   lds_barrier();
   frags(st0, 0, 0);

@@ -45,7 +45,7 @@ def gpu_rollout(name, actions):
     return to_np(zp)
 
 
-@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12)])
+@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("oddk", 9)])
 def test_rollout_matches_oracle(gpu_lib, name, n):
     from cem_jepa_predictor_amd import inputs
 
