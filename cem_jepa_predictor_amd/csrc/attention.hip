@@ -33,7 +33,7 @@ constexpr int kDh = 64;
 constexpr int kMaxTilesPerWave = 5;  // 16-row query tiles per wave -> B <= 320
 constexpr int kMaxKeyTiles = 20;     // 16-key tiles per staged block -> B <= 320
 
-__host__ __device__ __forceinline__ int kpad_of(int B) { return (B + 31) & ~31; }
+constexpr __host__ __device__ int kpad_of(int B) { return (B + 31) & ~31; }
 __host__ __device__ __forceinline__ int vt_ld_of(int B) { return kpad_of(B) + 8; }
 __host__ __device__ __forceinline__ int lds_bytes_of(int B) {
   return kpad_of(B) * kDh * 2 + kDh * vt_ld_of(B) * 2;
@@ -56,7 +56,7 @@ __device__ __forceinline__ float wave_sum_q(float v) {
 // max, exponentiates once and finishes before the next tile.
 // KT = ceil(B / 16): 16-key (and 16-query) tiles per block, fixed per model.
 template <int KT>
-__global__ __launch_bounds__(256) void attn_bf16_single_kernel(AttnArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_bf16_single_kernel(AttnArgs p) {
   constexpr int kKT2 = 2 * ((KT + 1) / 2);   // key tiles rounded up to MFMA k = 32 pairs
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int B = p.B, kpad = kpad_of(B), vld = vt_ld_of(B);
@@ -69,21 +69,38 @@ __global__ __launch_bounds__(256) void attn_bf16_single_kernel(AttnArgs p) {
   const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
 
   const bf16* kvb = static_cast<const bf16*>(p.kv[0]) + (long long)n * B * p.ldkv + h * kDh;
-  // ---- K: 8 lanes per 128-byte key row (coalesced), 16-byte swizzled LDS stores
-  for (int item = tid; item < kpad * 8; item += 256) {
-    const int kr = item >> 3, ck = item & 7;
-    const uint4 v = *reinterpret_cast<const uint4*>(kvb + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
-    *reinterpret_cast<uint4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = v;
-  }
-  // ---- V: a wave takes 16 keys x 4 chunks, so each transposed 2-byte store
-  // instruction writes 4 Vt rows x 32 contiguous bytes on distinct banks
-  for (int item = tid; item < kpad * 8; item += 256) {
-    const int kr = (item & 15) + 16 * (item >> 7);
-    const int ck = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
-    const uint4 v = *reinterpret_cast<const uint4*>(kvb + p.d + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
-    const bf16* ve = reinterpret_cast<const bf16*>(&v);
+  // Staging: every K and V load of this thread is issued before any LDS store, so
+  // the loads' latencies overlap instead of adding up.
+  // K: 8 lanes per 128-byte key row (coalesced), 16-byte swizzled LDS stores.
+  // V: a wave takes 16 keys x 4 chunks, so each transposed 2-byte store
+  // instruction writes 4 Vt rows x 32 contiguous bytes on distinct banks.
+  constexpr int kItems = (kpad_of(16 * KT) * 8 + 255) / 256;   // per thread, K and V each
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u32x4 kreg[kItems], vreg[kItems];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vt_lds[(ck * 8 + e) * vld + kr] = ve[e];
+  for (int it = 0; it < kItems; ++it) {
+    const int item = tid + 256 * it;
+    const int kr = item >> 3, ck = item & 7;
+    const int vr = (item & 15) + 16 * (item >> 7);
+    const int vc = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
+    if (item < kpad * 8) {
+      kreg[it] = *reinterpret_cast<const u32x4*>(kvb + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
+      vreg[it] = *reinterpret_cast<const u32x4*>(kvb + p.d + (long long)min(vr, B - 1) * p.ldkv + vc * 8);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first LDS store
+#pragma unroll
+  for (int it = 0; it < kItems; ++it) {
+    const int item = tid + 256 * it;
+    if (item < kpad * 8) {
+      const int kr = item >> 3, ck = item & 7;
+      *reinterpret_cast<u32x4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = kreg[it];
+      const int vr = (item & 15) + 16 * (item >> 7);
+      const int vc = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        vt_lds[(vc * 8 + e) * vld + vr] = static_cast<bf16>((vreg[it][e >> 1] >> (16 * (e & 1))) & 0xffffu);
+    }
   }
   __syncthreads();
 
@@ -113,8 +130,9 @@ __global__ __launch_bounds__(256) void attn_bf16_single_kernel(AttnArgs p) {
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          // only the last key tile can hold padding keys
-          const float v = (kt < KT - 1 || kt * 16 + 4 * g + r < B) ? acc[r] * sl2 : -INFINITY;
+          // only the last key tile can hold padding keys; scores stay unscaled
+          // here (the scale is positive, so it commutes with the max)
+          const float v = (kt < KT - 1 || kt * 16 + 4 * g + r < B) ? acc[r] : -INFINITY;
           st[kt][r] = v;
           bmax = fmaxf(bmax, v);
         }
@@ -122,13 +140,14 @@ __global__ __launch_bounds__(256) void attn_bf16_single_kernel(AttnArgs p) {
       // bound how many K fragments the scheduler keeps in flight (register pressure)
       if ((kt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    bmax = wave_max_q(bmax);
+    // p = exp((s - max) scale) = 2^(s sl2 - max sl2): one fma per score
+    const float nmax = -wave_max_q(bmax) * sl2;
     float psum = 0.f;
 #pragma unroll
     for (int kt = 0; kt < kKT2; ++kt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(st[kt][r] - bmax);
+        const float e = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, nmax));
         st[kt][r] = e;
         psum += e;
       }
