@@ -88,6 +88,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       vreg[it] = *reinterpret_cast<const u32x4*>(kvb + p.d + (long long)min(vr, B - 1) * p.ldkv + vc * 8);
     }
   }
+  // this wave's query fragments (tiles wave, wave + 4, ...), fetched with K and V
+  constexpr int kTilesPerWave = (KT + 3) / 4;
+  const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
+  bf16x8_t qall[kTilesPerWave][2];
+#pragma unroll
+  for (int ti = 0; ti < kTilesPerWave; ++ti) {
+    const int qr = min((wave + 4 * ti) * 16 + ql, B - 1);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      qall[ti][s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+  }
   __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first LDS store
 #pragma unroll
   for (int it = 0; it < kItems; ++it) {
@@ -104,15 +115,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   }
   __syncthreads();
 
-  const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
   bf16* obase = static_cast<bf16*>(p.o) + (long long)n * B * p.ldo + h * kDh;
-#pragma unroll 1
-  for (int tile = wave; tile < KT; tile += 4) {
-    const int qr = min(tile * 16 + ql, B - 1);
-    bf16x8_t qf[2];
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-      qf[s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+  for (int ti = 0; ti < kTilesPerWave; ++ti) {
+    const int tile = wave + 4 * ti;
+    if (tile >= KT) break;
+    const bf16x8_t* const qf = qall[ti];
     // S^T[key][q]: lane holds keys 16 kt + 4 g + r of query ql
     f32x4_t st[kKT2];
     float bmax = -INFINITY;
