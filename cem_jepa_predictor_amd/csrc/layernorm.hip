@@ -8,7 +8,8 @@
 // two-pass in registers; y = (x - mean) * rsqrt(var + eps) * g + b.
 //
 // One 64-lane wavefront per row; each lane owns 2*NCH elements as NCH pairs
-// (d = 128 * NCH).  HBM-bound: reads d and writes d elements per row.
+// (d = 128 * NCH), or for bf16 rows with d % 512 == 0, runs of 8 elements moved
+// with 16-byte accesses.  HBM-bound: reads d and writes d elements per row.
 #include "kernels.hpp"
 
 namespace cem {
@@ -73,6 +74,58 @@ __global__ __launch_bounds__(256) void layernorm_kernel(const T* __restrict__ x,
   }
 }
 
+// bf16 rows with d = 512 * NC: each lane owns NC runs of 8 consecutive elements
+// (16-byte loads and stores, one 1 KB wave access per run).
+template <int NC>
+__global__ __launch_bounds__(256) void layernorm_bf16x8_kernel(const bf16* __restrict__ x, int rows,
+                                                               RowMap in_rows,
+                                                               const float* __restrict__ g,
+                                                               const float* __restrict__ b, float eps,
+                                                               bf16* __restrict__ y) {
+  constexpr int d = 512 * NC;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + in_rows(r) * (long long)d);
+  float v[8 * NC];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint4 u = src[c * 64 + lane];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+      v[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      s += v[8 * c + 2 * k] + v[8 * c + 2 * k + 1];
+    }
+  }
+  const float mean = wave_sum(s) * (1.0f / d);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8 * NC; ++i) {
+    const float t = v[i] - mean;
+    q += t * t;
+  }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / d) + eps);
+  uint4* dst = reinterpret_cast<uint4*>(y + (long long)r * d);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float4 g0 = g4[(c * 64 + lane) * 2], g1 = g4[(c * 64 + lane) * 2 + 1];
+    const float4 b0 = b4[(c * 64 + lane) * 2], b1 = b4[(c * 64 + lane) * 2 + 1];
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+    uint32_t o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      o[k] = pack_bf16x2((v[8 * c + 2 * k] - mean) * rstd * gg[2 * k] + bb[2 * k],
+                         (v[8 * c + 2 * k + 1] - mean) * rstd * gg[2 * k + 1] + bb[2 * k + 1]);
+    dst[c * 64 + lane] = make_uint4(o[0], o[1], o[2], o[3]);
+  }
+}
+
 template <int NCH, typename T>
 hipError_t run(const T* x, int rows, RowMap in_rows, const float* g, const float* b, float eps,
                T* y, hipStream_t stream) {
@@ -94,6 +147,22 @@ template <typename T>
 hipError_t launch_layernorm(const T* x, int rows, int d, RowMap in_rows, const float* g,
                             const float* b, float eps, T* y, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
+  if constexpr (sizeof(T) == 2) {
+    // 16-byte path: x rows (and so g, b, y) are 16-byte aligned when d % 512 == 0
+    const int grid = (rows + 3) / 4;
+    if (d == 1024) {
+      layernorm_bf16x8_kernel<2><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y);
+      return hipGetLastError();
+    }
+    if (d == 512) {
+      layernorm_bf16x8_kernel<1><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y);
+      return hipGetLastError();
+    }
+    if (d == 2048) {
+      layernorm_bf16x8_kernel<4><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y);
+      return hipGetLastError();
+    }
+  }
   switch (d) {
     case 128: return run<1>(x, rows, in_rows, g, b, eps, y, stream);
     case 256: return run<2>(x, rows, in_rows, g, b, eps, y, stream);
