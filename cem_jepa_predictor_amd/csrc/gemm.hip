@@ -149,6 +149,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
                                                          int M, int N, int K, Epilogue epi) {
   __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) float bias_lds[BN];   // this tile's bias columns
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -250,11 +251,30 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   u32x4 g0[16], g1[16];
   gload(g0, 0, 0, 16);
   gload(g1, 1, 0, 16);
+  // the tile's bias columns go to LDS once, so the epilogue reads them at LDS latency
+  if (epi.bias && tid < BN / 4 && n0 + 4 * tid < N)
+    *reinterpret_cast<float4*>(bias_lds + 4 * tid) = *reinterpret_cast<const float4*>(epi.bias + n0 + 4 * tid);
   CEM_FENCE;
   lstore(g0, st0, 0, 16);
   CEM_FENCE;
   lds_barrier();
   frags(st0, 0, 0);
+  // The accumulators start at the bias (each lane's quads are 4 consecutive
+  // output columns), so no epilogue adds it.  Columns past N are never stored.
+  if (epi.bias) {
+    const float* const bl = bias_lds + wn * 128 + 4 * fk;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float4 bb = *reinterpret_cast<const float4*>(bl + j * 32 + 8 * q);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[i][j][4 * q] = bb.x; acc[i][j][4 * q + 1] = bb.y;
+          acc[i][j][4 * q + 2] = bb.z; acc[i][j][4 * q + 3] = bb.w;
+        }
+      }
+  }
   CEM_FENCE;
   for (int kt = 0; kt < KT; kt += 2) {
     slab(st0, st1, g1, g0, kt);       // slab kt+1 from g1 into st1; slab kt+2 loads into g0
@@ -272,7 +292,6 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       epi.rows.group >= 4 && ((uintptr_t)cbase & 15) == 0) {
     lds_barrier();   // every wave is done with the operand stages
     uint8_t* const ep = (wave < 2 ? st0 : st1) + (wave & 1) * 32768;
-    const float* const bias = epi.bias + ncol;
     bf16* const cwave = cbase + (n0 + wn * 128 - cshift);
     const int row_base = m0 + wm * 128;
     // destination rows of one lane, advanced incrementally (row map group >= 4)
@@ -289,6 +308,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       w.rem += d;
       if (w.rem >= epi.rows.group) { w.rem -= epi.rows.group; ++w.quot; }
     };
+    // a row map whose group exceeds M sends row m to m + offset
+    const bool plain_rows = epi.rows.group > M;
     if constexpr (KIND != kEpiResidual) {
       // bf16 staging: row r (256 bytes) holds 16-byte chunk c at c ^ (r & 15)
 #pragma unroll
@@ -298,9 +319,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
         for (int j = 0; j < 4; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float4 bb = *reinterpret_cast<const float4*>(bias + j * 32 + 8 * q);
-            float v[4] = {acc[i][j][4 * q] + bb.x, acc[i][j][4 * q + 1] + bb.y,
-                          acc[i][j][4 * q + 2] + bb.z, acc[i][j][4 * q + 3] + bb.w};
+            float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]};
             if constexpr (KIND == kEpiGelu) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = gelu_bf16_path(v[e]);
@@ -315,13 +335,21 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's staging writes are done
       const int c16 = lane & 15;
-      RowWalk w = row_walk(lane >> 4);
+      auto store_rows = [&](auto row_ptr) {
 #pragma unroll 4
-      for (int t = 0; t < 32; ++t) {
-        const int r = 4 * t + (lane >> 4);
-        const uint4 d = *reinterpret_cast<const uint4*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4));
-        if (row_base + r < M) *reinterpret_cast<uint4*>(cwave + row_of(w) * ldc + c16 * 8) = d;
-        row_step(w, 4);
+        for (int t = 0; t < 32; ++t) {
+          const int r = 4 * t + (lane >> 4);
+          const uint4 d = *reinterpret_cast<const uint4*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4));
+          bf16* const dst = row_ptr(t);
+          if (row_base + r < M) *reinterpret_cast<uint4*>(dst + c16 * 8) = d;
+        }
+      };
+      if (plain_rows) {
+        bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + (lane >> 4)) * ldc;
+        store_rows([&](int t) { return p0 + (long long)(4 * t) * ldc; });
+      } else {
+        RowWalk w = row_walk(lane >> 4);
+        store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 4); return q; });
       }
     } else {
       // fp32 staging in two 64-row halves (row r: 512 bytes, 16-byte chunk c at
@@ -331,16 +359,21 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint2 res[32];
-        {
-          RowWalk w = row_walk(64 * h + (lane >> 5));
+        auto load_rows = [&](auto row_ptr) {
 #pragma unroll
           for (int t = 0; t < 32; ++t) {
             const int r = 64 * h + 2 * t + (lane >> 5);
+            const bf16* const src = row_ptr(t);
             res[t] = make_uint2(0u, 0u);
-            if (row_base + r < M)
-              res[t] = *reinterpret_cast<const uint2*>(cwave + row_of(w) * ldc + ch * 4);
-            row_step(w, 2);
+            if (row_base + r < M) res[t] = *reinterpret_cast<const uint2*>(src + ch * 4);
           }
+        };
+        if (plain_rows) {
+          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 5)) * ldc;
+          load_rows([&](int t) { return p0 + (long long)(2 * t) * ldc; });
+        } else {
+          RowWalk w = row_walk(64 * h + (lane >> 5));
+          load_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 2); return q; });
         }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
@@ -350,27 +383,34 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-              const float4 bb = *reinterpret_cast<const float4*>(bias + j * 32 + 8 * q);
-              const float4 v = make_float4(acc[i][j][4 * q] + bb.x, acc[i][j][4 * q + 1] + bb.y,
-                                           acc[i][j][4 * q + 2] + bb.z, acc[i][j][4 * q + 3] + bb.w);
+              const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
+                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
               const int cw = 8 * j + 2 * q + fk;
               *reinterpret_cast<float4*>(ep + r * 512 + ((cw ^ (r & 15)) << 4)) = v;
             }
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
-        RowWalk w = row_walk(64 * h + (lane >> 5));
+        auto store_rows = [&](auto row_ptr) {
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-          const int r = 2 * t + (lane >> 5);
-          const float4 f = *reinterpret_cast<const float4*>(ep + r * 512 + ((ch ^ (r & 15)) << 4));
-          if (row_base + 64 * h + r < M) {
-            const uint2 u = res[t];
-            float v[4] = {__uint_as_float(u.x << 16) + f.x, __uint_as_float(u.x & 0xffff0000u) + f.y,
-                          __uint_as_float(u.y << 16) + f.z, __uint_as_float(u.y & 0xffff0000u) + f.w};
-            Store4<bf16>::store(cwave + row_of(w) * ldc + ch * 4, v);
+          for (int t = 0; t < 32; ++t) {
+            const int r = 2 * t + (lane >> 5);
+            const float4 f = *reinterpret_cast<const float4*>(ep + r * 512 + ((ch ^ (r & 15)) << 4));
+            bf16* const dst = row_ptr(t);
+            if (row_base + 64 * h + r < M) {
+              const uint2 u = res[t];
+              float v[4] = {__uint_as_float(u.x << 16) + f.x, __uint_as_float(u.x & 0xffff0000u) + f.y,
+                            __uint_as_float(u.y << 16) + f.z, __uint_as_float(u.y & 0xffff0000u) + f.w};
+              Store4<bf16>::store(dst + ch * 4, v);
+            }
           }
-          row_step(w, 2);
+        };
+        if (plain_rows) {
+          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 5)) * ldc;
+          store_rows([&](int t) { return p0 + (long long)(2 * t) * ldc; });
+        } else {
+          RowWalk w = row_walk(64 * h + (lane >> 5));
+          store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 2); return q; });
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);   // this half's reads are done before the next overwrites it
         __builtin_amdgcn_sched_barrier(0);
@@ -378,6 +418,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     }
     return;
   }
+  Epilogue e_nb = epi;
+  e_nb.bias = nullptr;   // already in the accumulators
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int m = m0 + wm * 128 + i * 32 + fr;
@@ -389,7 +431,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       for (int q = 0; q < 4; ++q) {
         float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                       acc[i][j][4 * q + 3]};
-        epilogue_row4<bf16, KIND>(epi, N, row, ncol + j * 32 + 8 * q, v);
+        epilogue_row4<bf16, KIND>(e_nb, N, row, ncol + j * 32 + 8 * q, v);
       }
   }
 }
