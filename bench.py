@@ -38,8 +38,8 @@ MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (reference for fp32 models)
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
 # as null once those change.
 GEMM_COUNTERS = {
-    "sources_sha256": "8f2db56b3fe39ecdc6b7ac168c7ce013e527c7747cf71586298c9d35b3e9c25a",
-    "bytes_per_launch": 4236798648,
+    "sources_sha256": "43ee756b32331a68871871017476aaa0ed04bbd7361fb718eb15fd5b50783290",
+    "bytes_per_launch": 3735451950,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 
