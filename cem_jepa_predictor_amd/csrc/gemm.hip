@@ -280,7 +280,6 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     slab(st0, st1, g1, g0, kt);       // slab kt+1 from g1 into st1; slab kt+2 loads into g0
     slab(st1, st0, g0, g1, kt + 1);
   }
-  __builtin_amdgcn_s_waitcnt(0x0070);   // no load outlives the main loop
 #undef CEM_FENCE
 
   const int ncol = n0 + wn * 128 + 4 * fk;
@@ -290,7 +289,9 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int cshift = to_c0 ? 0 : epi.split;
   if ((to_c0 || to_c1) && n0 + BN <= N && epi.bias && (ldc & 7) == 0 && (cshift & 7) == 0 &&
       epi.rows.group >= 4 && ((uintptr_t)cbase & 15) == 0) {
-    lds_barrier();   // every wave is done with the operand stages
+    // No barrier: after the last slab's barrier the operand stages see only
+    // fragment reads whose values are never used, and each wave stages into its
+    // own 32 KB, so a wave starts its epilogue as soon as its MFMAs are issued.
     uint8_t* const ep = (wave < 2 ? st0 : st1) + (wave & 1) * 32768;
     bf16* const cwave = cbase + (n0 + wn * 128 - cshift);
     const int row_base = m0 + wm * 128;
@@ -336,12 +337,18 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's staging writes are done
       const int c16 = lane & 15;
       auto store_rows = [&](auto row_ptr) {
-#pragma unroll 4
+        // all 32 row pieces come out of LDS first, so the stores issue back to back
+        u32x4 d[32];
+#pragma unroll
         for (int t = 0; t < 32; ++t) {
           const int r = 4 * t + (lane >> 4);
-          const uint4 d = *reinterpret_cast<const uint4*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4));
+          d[t] = *reinterpret_cast<const u32x4*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4));
+        }
+#pragma unroll
+        for (int t = 0; t < 32; ++t) {
+          const int r = 4 * t + (lane >> 4);
           bf16* const dst = row_ptr(t);
-          if (row_base + r < M) *reinterpret_cast<uint4*>(dst + c16 * 8) = d;
+          if (row_base + r < M) *reinterpret_cast<u32x4*>(dst + c16 * 8) = d[t];
         }
       };
       if (plain_rows) {
