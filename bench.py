@@ -117,6 +117,41 @@ def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+HBM_PEAK_BYTES_PER_S = 8.0e12
+
+
+def plan_roofline_ms(m, pc, peak_tflops: float) -> float:
+    """Per-kernel roofline of one plan step: the sum over kernels of
+    max(FLOPs / MFMA peak, bytes / HBM peak), each activation read or written once
+    per kernel, LayerNorm folded into the projections (no separate pass), KV-cached
+    block-causal attention counted on its unmasked part only."""
+    es = 2 if m.dtype == "bf16" else 4
+    peak = peak_tflops * 1e12
+    N, R, H = pc.n_samples, pc.rounds, pc.horizon
+    B, P, E, d, F, L = m.patches + 2, m.patches, m.enc_dim, m.d_model, m.d_mlp, m.layers
+    M = N * B
+
+    def gemm(rows, n, k, residual=False):
+        flop = 2.0 * rows * n * k
+        byts = es * (rows * k + n * k + rows * n * (2 if residual else 1))
+        return max(flop / peak, byts / HBM_PEAK_BYTES_PER_S)
+
+    total = gemm(P, d, E)                                   # frame in-projection, once per plan
+    per_round = 0.0
+    for t in range(H):
+        if t > 0:
+            per_round += gemm(N * P, d, E)                  # in-projection of the fed-back frame
+        for _ in range(L):
+            per_round += gemm(M, 3 * d, d) + gemm(M, d, d, True) + gemm(M, F, d) + gemm(M, d, F, True)
+            kv = (t + 1) * B
+            flop = 4.0 * N * B * kv * d
+            byts = es * N * (B * d + 2 * kv * d + B * d)
+            per_round += max(flop / peak, byts / HBM_PEAK_BYTES_PER_S)
+        per_round += gemm(N * P, E, d)                      # out-projection
+    per_round += (N * P * E * es + P * E * 4) / HBM_PEAK_BYTES_PER_S   # L1 energy
+    return (total + R * per_round) * 1e3
+
+
 def cpu_baseline(wl, sample_seconds: float):
     """Time the oracle on the host: whole candidates through the predictor + energy,
     then the per-round search bookkeeping, extrapolated to candidate-evals/s."""
@@ -150,6 +185,16 @@ def cpu_baseline(wl, sample_seconds: float):
             break
     t_eval = time.perf_counter() - t0
     evals_per_s = done / t_eval
+    # the same rollout on one thread (at least one candidate)
+    one_core = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(1):
+            t2 = time.perf_counter()
+            o_energy.energy_l1(pred.rollout_cached(x[:1], z_obs, s0), z_goal)
+            one_core = 1.0 / (time.perf_counter() - t2)
+    except ImportError:  # pragma: no cover
+        pass
     # search bookkeeping of one full plan (sample + select + refit for every round)
     t1 = time.perf_counter()
     e = np.random.default_rng(0).standard_normal(pc.n_samples)
@@ -161,6 +206,7 @@ def cpu_baseline(wl, sample_seconds: float):
     plan_s = pc.n_samples * pc.rounds / evals_per_s + t_book
     return {"value": round(evals_per_s, 6), "unit": "candidate-evals/s", "cores": int(threads),
             "kind": "oracle",
+            "one_core_value": round(one_core, 6) if one_core else None,
             "sample": (f"{done} candidate rollouts + L1 energies of the {wl.name} workload in "
                        f"{t_eval:.1f} s (NumPy float64), plus one plan's sampling/top-K/refit "
                        f"({t_book * 1e3:.1f} ms); extrapolated plan step {plan_s:.0f} s")}
@@ -169,8 +215,10 @@ def cpu_baseline(wl, sample_seconds: float):
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--timer-steps", type=int, default=5,
+                    help="eager steps with the library's GEMM timers (roofline.achieved)")
     ap.add_argument("--workload", default="vjepa2ac")
     ap.add_argument("--samples", type=int, default=0, help="override N (sweep); K = N / 10")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -256,16 +304,22 @@ def main() -> int:
 
     # ---- timed region: K plan steps replayed from the captured graph
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     w0 = time.perf_counter()
     ev0.record(stream)
     for i in range(args.steps):
+        marks[i].record(stream)
         step(1000 + i)
+    marks[args.steps].record(stream)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms = ev0.elapsed_time(ev1) / args.steps
-    eprint(f"[bench] timed {args.steps} steps: {ms:.2f} ms/step (wall {wall:.2f} s)")
+    per_step = np.array([marks[i].elapsed_time(marks[i + 1]) for i in range(args.steps)])
+    p10, p50, p90 = (float(np.percentile(per_step, q)) for q in (10, 50, 90))
+    eprint(f"[bench] timed {args.steps} steps: {ms:.2f} ms/step (median {p50:.2f}, p10 {p10:.2f}, "
+           f"p90 {p90:.2f}; wall {wall:.2f} s)")
 
     # ---- kernel timers: the same K steps enqueued directly with HIP events around
     # every dense-GEMM launch, on the stream the kernels run on
@@ -273,13 +327,14 @@ def main() -> int:
     eager_ms = None
     if not args.no_kernel_timers:
         model.timer_enable(True)
+        nt = max(1, min(args.steps, args.timer_steps))
         torch.cuda.synchronize()
         ev0.record(stream)
-        for i in range(args.steps):
+        for i in range(nt):
             step(1000 + i, use_graph=False)
         ev1.record(stream)
         torch.cuda.synchronize()
-        eager_ms = ev0.elapsed_time(ev1) / args.steps
+        eager_ms = ev0.elapsed_time(ev1) / nt
         launches, gemm_ms, flop = model.timer_read()
         model.timer_enable(False)
         peak = MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -293,8 +348,8 @@ def main() -> int:
                                 "copy-calibrated)",
                 "kernel": "gemm_bf16_kernel" if m.dtype == "bf16" else "gemm_f32_kernel",
                 "launches": launches, "avg_launch_ms": round(gemm_ms / max(launches, 1), 4),
-                "gemm_share_of_step": round(gemm_ms / args.steps / eager_ms, 4)}
-        eprint(f"[bench] GEMMs: {launches} launches, {gemm_ms / args.steps:.2f} ms/step, "
+                "gemm_share_of_step": round(gemm_ms / nt / eager_ms, 4)}
+        eprint(f"[bench] GEMMs: {launches} launches, {gemm_ms / nt:.2f} ms/step, "
                f"{achieved:.1f} TFLOP/s; eager step {eager_ms:.2f} ms")
 
     cpu = None
@@ -303,6 +358,7 @@ def main() -> int:
         cpu = cpu_baseline(wl, args.cpu_seconds)
 
     value = N * R / (ms * 1e-3)
+    plan_ms_roof = plan_roofline_ms(m, pc, MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS)
     out = {
         "metric": "predictor candidate-evals/sec + ms per CEM plan step (800x10) on 1 MI355X",
         "value": round(value, 2), "unit": "candidate-evals/s", "n_gpus": 1, "steps": args.steps,
@@ -314,6 +370,10 @@ def main() -> int:
                    "layers": m.layers, "d_model": m.d_model, "heads": m.heads, "d_mlp": m.d_mlp,
                    "patches": m.patches, "enc_dim": m.enc_dim, "graph_replay": True,
                    "eager_ms_per_step": round(eager_ms, 3) if eager_ms else None},
+        "ms_per_step_p10": round(p10, 3), "ms_per_step_median": round(p50, 3),
+        "ms_per_step_p90": round(p90, 3),
+        "plan_roofline_ms": round(plan_ms_roof, 1),
+        "plan_roofline_frac": round(plan_ms_roof / ms, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
     }
