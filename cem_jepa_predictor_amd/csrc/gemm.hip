@@ -8,30 +8,38 @@
 // action), so the bf16 kernel is MFMA-bound by design.
 //
 // bf16 kernel (gfx950):
-//  * 256 x 256 output tile per 256-thread workgroup, BK = 64; four wave64s in
-//    a 2 x 2 grid, each owning a 128 x 128 sub-tile = 4 x 4 tiles of
-//    v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+//  * 256 x 256 output tile per 512-thread workgroup: eight wave64s in a 2 x 4
+//    grid, two per SIMD, each owning a 128 x 64 sub-tile = 4 x 2 tiles of
+//    v_mfma_f32_32x32x16_bf16 (128 fp32 accumulators per lane).  With two
+//    waves on a SIMD, one wave's MFMAs issue while the other waits on a load
+//    or an LDS read; a single wave per SIMD spends most of a K-slab stalled
+//    on its own memory instructions.
 //  * The MFMA's first operand is the weight tile and its second the
 //    activation tile, so each lane's accumulator quads hold 4 consecutive
 //    output columns of one output row.
-//  * Operands: global -> VGPR (buffer_load_dwordx4, two staging register sets)
-//    -> LDS double buffer (2 x 64 KB), memory two slabs ahead of the MFMAs,
-//    every memory instruction placed between MFMAs (see the main loop).
-//    128-byte LDS rows hold their eight 16-byte chunks at c ^ ((r >> 1) & 7),
-//    so fragment reads are free of bank conflicts.
+//  * Operands: global -> LDS directly (buffer_load_dwordx4 ... lds, no VGPR
+//    staging) through a ring of 5 stages of BK = 32 (32 KB each: A and B slabs),
+//    three slabs in flight ahead of the one being read.  64-byte LDS rows hold
+//    their four 16-byte k-chunks at c ^ ((r >> 2) & 3), so fragment reads are
+//    free of bank conflicts; each lane loads the chunk that belongs at its slot.
+//  * One barrier per K-slab, in the middle of the slab: it publishes slab
+//    kt+1 and frees slab kt-1's stage, so fragment reads never wait on it.
+//    Every MFMA, fragment read and load is placed explicitly (scheduling
+//    fences between single instructions).
 //  * Block -> tile map is XCD-aware: the dispatcher hands block b to XCD
 //    b % 8, so each XCD receives a contiguous range of logical tiles, ordered
 //    in groups of 8 row-tiles to share A and B panels in that XCD's L2.
 //  * Ragged M / N: operand loads go through buffer resources bounded at the
 //    tile's last valid row (the hardware returns zero beyond it), stores are
-//    masked.
-//  * Results leave through LDS as full rows (see the epilogue).
+//    masked.  K must be a multiple of 32.
+//  * Results leave through LDS as full 128-byte row pieces (see the epilogue).
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
 //    each carries only its own epilogue code.
 //
-// Epilogue (fp32): + bias, optional GELU, optional residual add (the
-// output already holds the residual stream), optional column split into two
-// destinations (q -> Q buffer, k|v -> KV cache), optional output-row remap.
+// Epilogue (fp32): + bias (preloaded into the accumulators), optional GELU,
+// optional residual add (the output already holds the residual stream),
+// optional column split into two destinations (q -> Q buffer, k|v -> KV
+// cache), optional output-row remap.
 #include "kernels.hpp"
 
 namespace cem {
@@ -92,9 +100,12 @@ __device__ __forceinline__ void epilogue_row4(const Epilogue& e, int N, long lon
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-constexpr int BM = 256, BN = 256, BK = 64, NTHR = 256;
-constexpr int TILE_BYTES = BM * BK * 2;       // 32 KB per operand slab
-constexpr int STAGE_BYTES = 2 * TILE_BYTES;   // A slab + B slab
+constexpr int BM = 256, BN = 256, BK = 32, NTHR = 512;
+constexpr int NS = 5;                       // LDS stages in the operand ring
+constexpr int LEAD = NS - 2;                // slabs in flight ahead of the one being read
+constexpr int OPB = BM * BK * 2;            // 16 KB: one operand slab (256 rows x 64 B)
+constexpr int STB = 2 * OPB;                // 32 KB: A slab + B slab
+constexpr int DMA_PER_WAVE = 4;             // 1 KB instructions per wave per slab (2 A + 2 B)
 constexpr int GROUP_M = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -113,9 +124,6 @@ __device__ __forceinline__ void tile_of_block(int b, int nb, int tiles_m, int ti
   tn = in / gsize;
 }
 
-// Buffer resource over rows [row0, row0 + rows) of a row-major bf16 matrix,
-// advanced by k elements; loads past the last valid row return zero.
-// Valid rows stay in range for every k < K <= ld: r * ld * 2 + 2k + 16 <= rows * ld * 2.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, int row0, int rows,
                                                             int ld, int k) {
   const uint32_t bytes = (uint32_t)rows * (uint32_t)ld * 2u - (uint32_t)k * 2u;
@@ -125,31 +133,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, in
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Main loop.  Operand slabs (BK = 64 columns of 256 A rows and 256 B rows,
-// 128 contiguous bytes per row) go global -> VGPR -> LDS through two staging
-// register sets, so memory runs two slabs ahead of the MFMAs without a third
-// LDS stage: during slab kt the wave issues slab kt+2's loads (4 per substep)
-// and writes slab kt+1 (loaded during slab kt-1) into the free LDS stage
-// (substeps 0-2), each interleaved one per MFMA so no burst of memory
-// instructions holds up MFMA issue.  One barrier per slab, before the last
-// substep's MFMAs; it waits for LDS traffic only.  Loads of slabs at or past K
-// use an empty buffer resource (zeros, no memory traffic), which keeps every
-// slab of the loop identical; an odd slab count runs one extra all-zero slab.
-//
-// Epilogue.  When a tile maps to one destination with 16-byte aligned rows,
-// each wave stages its 128 x 128 result in 32 KB of the freed operand LDS and
-// then writes full rows (16 bytes a lane, 4 rows x 256 bytes per
-// instruction) instead of 16-byte pieces of 32 rows.  Plain / GELU values are
-// staged as bf16 (rounded once, as before); the residual kind stages fp32 in
-// two 64-row halves and adds the residual rows, loaded first, in fp32, so it
-// also rounds once.  Other tiles take the per-4-column path.
 template <int KIND>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
                                                          const bf16* __restrict__ Bt, int ldb,
                                                          int M, int N, int K, Epilogue epi) {
-  __shared__ __attribute__((aligned(1024))) uint8_t st0[STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t st1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) float bias_lds[BN];   // this tile's bias columns
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -157,117 +145,66 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
-
-  // Global loads: wave instruction j covers rows 8 (4 j + wave) .. +7 of an operand
-  // slab, lane l row + l / 8, logical 16-byte chunk l % 8.  LDS row r holds its
-  // logical chunk c at position c ^ ((r >> 1) & 7): a b128 fragment read is served
-  // 16 lanes (rows r..r+15) per pass over 64 four-byte banks, and (row parity,
-  // (r >> 1) & 7) gives those 16 rows 16 distinct bank groups.  Rows
-  // 8 (4 j + wave) + lrow have (r >> 1) & 7 = (4 (wave & 1) + (lrow >> 1)) & 7.
-  const int lrow = lane >> 3, lc = lane & 7;
-  const int sw = (4 * (wave & 1) + (lrow >> 1)) & 7;
-  const int goff_a = (8 * wave + lrow) * lda * 2 + lc * 16, gstep_a = 32 * lda * 2;
-  const int goff_b = (8 * wave + lrow) * ldb * 2 + lc * 16, gstep_b = 32 * ldb * 2;
-  const int lds_w = (8 * wave + lrow) * 128 + ((lc ^ sw) << 4);
   const int KT = K / BK;
-  // part p < 8: A rows of instruction p; p >= 8: B rows of instruction p - 8.
-  // The row offset stays in the range-checked VGPR offset (soffset is not checked).
-  auto gload = [&](u32x4* g, int kt, int p0, int p1) {
+
+  // Operand slabs: global -> LDS by buffer_load ... lds (16 bytes a lane; one
+  // instruction fills 1 KB of LDS, lane l at byte 16 l).  LDS row r (64 bytes,
+  // 4 chunks of 8 k-values) holds logical chunk c at position c ^ ((r >> 2) & 3),
+  // so each lane loads the chunk that belongs at its slot.  Wave w, instruction
+  // j < 2: local rows 32 w + 16 j + lane / 4 of A, then the same rows of B.
+  const int drow = 32 * wave + (lane >> 2);
+  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
+  const int voff_a = drow * lda * 2 + dchunk * 16, vstep_a = 16 * lda * 2;
+  const int voff_b = drow * ldb * 2 + dchunk * 16, vstep_b = 16 * ldb * 2;
+  auto dma = [&](int kt, int stage) {
     const bool live = kt < KT;
     const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, live ? rows_a : 0, lda, live ? kt * BK : 0);
     const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, live ? rows_b : 0, ldb, live ? kt * BK : 0);
+    uint8_t* const sa = lds + stage * STB + wave * 32 * 64;
 #pragma unroll
-    for (int p = p0; p < p1; ++p) {
-      const int j = p & 7;
-      g[p] = (p < 8) ? __builtin_amdgcn_raw_buffer_load_b128(ra, goff_a + j * gstep_a, 0, 0)
-                     : __builtin_amdgcn_raw_buffer_load_b128(rb, goff_b + j * gstep_b, 0, 0);
-    }
-  };
-  auto lstore = [&](const u32x4* g, uint8_t* stage, int p0, int p1) {
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + j * 1024), 16, voff_a + j * vstep_a, 0, 0, 0);
 #pragma unroll
-    for (int p = p0; p < p1; ++p)
-      *reinterpret_cast<u32x4*>(stage + (p < 8 ? 0 : TILE_BYTES) + lds_w + (p & 7) * 4096) = g[p];
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sa + OPB + j * 1024), 16, voff_b + j * vstep_b, 0, 0, 0);
   };
 
-  // fragments: lane reads row (l % 32) of a 32-row MFMA tile, k half (l / 32)
-  const int wm = wave >> 1, wn = wave & 1;
+  // 8 waves in a 2 x 4 grid, wave (wm, wn) owns output rows 128 wm .. +127 and
+  // columns 64 wn .. +63: 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.
+  // Fragments: lane reads local row (l % 32) of a 32-row tile, k chunk 2 s + l / 32.
+  const int wm = wave >> 2, wn = wave & 3;
   const int fr = lane & 31, fk = lane >> 5;
-  const int arow = (wm * 128 + fr) * 128;
-  const int brow = TILE_BYTES + (wn * 128 + fr) * 128;
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
-  bf16x8_t fa[2][4], fb[2][4];
-  auto frags = [&](const uint8_t* stage, int s, int buf) {
-    const int pc = ((2 * s + fk) ^ ((fr >> 1) & 7)) << 4;
+  const int arow = (wm * 128 + fr) * 64;
+  const int brow = OPB + (wn * 64 + fr) * 64;
+  const int fsw = (fr >> 2) & 3;
+  f32x16_t acc[4][2];
+  bf16x8_t fa[2][4], fb[2][2];
+  auto frags = [&](int stage, int s, int buf) {
+    const uint8_t* st = lds + stage * STB;
+    const int pc = ((2 * s + fk) ^ fsw) << 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(stage + arow + i * 4096 + pc);
+      fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + arow + i * 2048 + pc);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(stage + brow + j * 4096 + pc);
+    for (int j = 0; j < 2; ++j)
+      fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + brow + j * 2048 + pc);
   };
   // The weight tile is the MFMA's first operand, so D[i][j] has j = output row
   // (lane % 32) and i = output column 8 (r / 4) + 4 (lane / 32) + r % 4.
-  auto mfma = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-  };
-  auto lds_barrier = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0); global loads stay in flight
-    __builtin_amdgcn_s_barrier();
-  };
-  // schedule of one substep: its 8 fragment reads first, then one LDS write and one
-  // global load after each of the first nw / nl MFMAs
-  auto interleave = [&](int nw, int nl) {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    for (int r = 0; r < 16; ++r) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      if (r < nw) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
-      if (r < nl) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-    }
-  };
+#define CEM_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
 #define CEM_FENCE __builtin_amdgcn_sched_barrier(0)
-  // One K-slab from `cur`: gw holds slab kt+1 (written to `nxt`), gl receives slab kt+2.
-  auto slab = [&](uint8_t* cur, uint8_t* nxt, u32x4* gw, u32x4* gl, int kt) {
-    frags(cur, 1, 1); lstore(gw, nxt, 0, 6); gload(gl, kt + 2, 0, 4); mfma(0); interleave(6, 4);
-    CEM_FENCE;
-    frags(cur, 2, 0); lstore(gw, nxt, 6, 11); gload(gl, kt + 2, 4, 8); mfma(1); interleave(5, 4);
-    CEM_FENCE;
-    frags(cur, 3, 1); lstore(gw, nxt, 11, 16); gload(gl, kt + 2, 8, 12); mfma(0); interleave(5, 4);
-    CEM_FENCE;
-    lds_barrier();
-    frags(nxt, 0, 0); gload(gl, kt + 2, 12, 16); mfma(1); interleave(0, 4);
-    CEM_FENCE;
-  };
-  // prologue: slabs 0 and 1 in flight together; slab 0 goes to LDS as it lands
-  u32x4 g0[16], g1[16];
-  gload(g0, 0, 0, 16);
-  gload(g1, 1, 0, 16);
-  // the tile's bias columns go to LDS once, so the epilogue reads them at LDS latency
-  if (epi.bias && tid < BN / 4 && n0 + 4 * tid < N)
-    *reinterpret_cast<float4*>(bias_lds + 4 * tid) = *reinterpret_cast<const float4*>(epi.bias + n0 + 4 * tid);
-  CEM_FENCE;
-  lstore(g0, st0, 0, 16);
-  CEM_FENCE;
-  lds_barrier();
-  frags(st0, 0, 0);
-  // The accumulators start at the bias (each lane's quads are 4 consecutive
-  // output columns), so no epilogue adds it.  Columns past N are never stored.
-  if (epi.bias) {
-    const float* const bl = bias_lds + wn * 128 + 4 * fk;
+
+  // accumulators start at the bias (lane quads are 4 consecutive output columns);
+  // the bias loads go first so their wait does not also wait for operand slabs
+  {
+    const int cb = n0 + wn * 64 + 4 * fk;
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float4 bb = *reinterpret_cast<const float4*>(bl + j * 32 + 8 * q);
+        const int c = cb + j * 32 + 8 * q;
+        float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (epi.bias && c < N) bb = *reinterpret_cast<const float4*>(epi.bias + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           acc[i][j][4 * q] = bb.x; acc[i][j][4 * q + 1] = bb.y;
@@ -276,26 +213,91 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       }
   }
   CEM_FENCE;
-  for (int kt = 0; kt < KT; kt += 2) {
-    slab(st0, st1, g1, g0, kt);       // slab kt+1 from g1 into st1; slab kt+2 loads into g0
-    slab(st1, st0, g0, g1, kt + 1);
+#pragma unroll
+  for (int s = 0; s <= LEAD; ++s) dma(s, s);
+  CEM_FENCE;
+  CEM_VMCNT(DMA_PER_WAVE * LEAD);   // slab 0 landed (this wave's part)
+  __builtin_amdgcn_s_barrier();
+  CEM_FENCE;
+  frags(0, 0, 0);
+  CEM_FENCE;
+  // Slab kt: MFMAs of k-substep 0 while substep 1's fragments are read; then
+  // wait for slab kt+1 and barrier (which also frees slab kt-1's stage for the
+  // load of slab kt+1+LEAD); MFMAs of substep 1 while slab kt+1's first
+  // fragments are read and this wave's share of slab kt+1+LEAD is requested.
+  // The pieces below are single instructions, placed one by one between
+  // scheduling fences.
+  auto mfma1 = [&](int buf, int idx) {
+    const int i = idx >> 1, j = idx & 1;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  auto frag1 = [&](int stage, int s, int buf, int r) {
+    const uint8_t* st = lds + stage * STB;
+    const int pc = ((2 * s + fk) ^ fsw) << 4;
+    if (r < 4) fa[buf][r] = *reinterpret_cast<const bf16x8_t*>(st + arow + r * 2048 + pc);
+    else fb[buf][r - 4] = *reinterpret_cast<const bf16x8_t*>(st + brow + (r - 4) * 2048 + pc);
+  };
+  auto dma1 = [&](int kt, int stage, int d) {
+    const bool live = kt < KT;
+    if (d < 2) {
+      const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, live ? rows_a : 0, lda, live ? kt * BK : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + stage * STB + wave * 32 * 64 + d * 1024), 16, voff_a + d * vstep_a, 0, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, live ? rows_b : 0, ldb, live ? kt * BK : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + stage * STB + OPB + wave * 32 * 64 + (d - 2) * 1024), 16, voff_b + (d - 2) * vstep_b, 0, 0, 0);
+    }
+  };
+#define F __builtin_amdgcn_sched_barrier(0)
+  int cur = 0, nxt = 1, fill = LEAD + 1;
+  for (int kt = 0; kt < KT; ++kt) {
+    // phase A: substep 0 MFMAs, substep 1 fragments read in between
+    mfma1(0, 0); F; frag1(cur, 1, 1, 0); F; frag1(cur, 1, 1, 1); F;
+    mfma1(0, 1); F; frag1(cur, 1, 1, 2); F; frag1(cur, 1, 1, 3); F;
+    mfma1(0, 2); F; frag1(cur, 1, 1, 4); F; frag1(cur, 1, 1, 5); F;
+    mfma1(0, 3); F;
+    mfma1(0, 4); F;
+    mfma1(0, 5); F;
+    mfma1(0, 6); F;
+    mfma1(0, 7); F;
+    // slab kt+1 landed everywhere; slab kt-1's stage is free for slab kt+1+LEAD
+    CEM_VMCNT(DMA_PER_WAVE * (LEAD - 1));
+    __builtin_amdgcn_s_barrier();
+    F;
+    // phase B: substep 1 MFMAs; slab kt+1's substep 0 fragments, then this wave's loads
+    mfma1(1, 0); F; frag1(nxt, 0, 0, 0); F; frag1(nxt, 0, 0, 1); F;
+    mfma1(1, 1); F; frag1(nxt, 0, 0, 2); F; frag1(nxt, 0, 0, 3); F;
+    mfma1(1, 2); F; frag1(nxt, 0, 0, 4); F; frag1(nxt, 0, 0, 5); F;
+    mfma1(1, 3); F;
+    dma1(kt + 1 + LEAD, fill, 0); F;
+    mfma1(1, 4); F;
+    dma1(kt + 1 + LEAD, fill, 1); F;
+    mfma1(1, 5); F;
+    dma1(kt + 1 + LEAD, fill, 2); F;
+    mfma1(1, 6); F;
+    dma1(kt + 1 + LEAD, fill, 3); F;
+    mfma1(1, 7); F;
+    cur = nxt; nxt = (nxt + 1 == NS) ? 0 : nxt + 1; fill = (fill + 1 == NS) ? 0 : fill + 1;
   }
+#undef F
+  CEM_VMCNT(0);
+  __builtin_amdgcn_s_barrier();   // every wave is done with the operand stages
+  CEM_FENCE;
 #undef CEM_FENCE
+#undef CEM_VMCNT
 
-  const int ncol = n0 + wn * 128 + 4 * fk;
+  const int ncol = n0 + wn * 64 + 4 * fk;
   const bool to_c0 = n0 + BN <= epi.split, to_c1 = n0 >= epi.split;
   bf16* const cbase = static_cast<bf16*>(to_c0 ? epi.c0 : epi.c1);
   const int ldc = to_c0 ? epi.ld0 : epi.ld1;
   const int cshift = to_c0 ? 0 : epi.split;
-  if ((to_c0 || to_c1) && n0 + BN <= N && epi.bias && (ldc & 7) == 0 && (cshift & 7) == 0 &&
-      epi.rows.group >= 4 && ((uintptr_t)cbase & 15) == 0) {
-    // No barrier: after the last slab's barrier the operand stages see only
-    // fragment reads whose values are never used, and each wave stages into its
-    // own 32 KB, so a wave starts its epilogue as soon as its MFMAs are issued.
-    uint8_t* const ep = (wave < 2 ? st0 : st1) + (wave & 1) * 32768;
-    bf16* const cwave = cbase + (n0 + wn * 128 - cshift);
+  if ((to_c0 || to_c1) && n0 + BN <= N && (ldc & 7) == 0 && (cshift & 7) == 0 &&
+      epi.rows.group >= 8 && ((uintptr_t)cbase & 15) == 0) {
+    // Each wave stages its 128 x 64 result in its own part of the freed operand
+    // LDS, then writes whole 128-byte row pieces (16 bytes a lane, 8 rows per
+    // store instruction).
+    uint8_t* const ep = lds + wave * 16384;
+    bf16* const cwave = cbase + (n0 + wn * 64 - cshift);
     const int row_base = m0 + wm * 128;
-    // destination rows of one lane, advanced incrementally (row map group >= 4)
     struct RowWalk {
       long long quot;
       int rem;
@@ -309,15 +311,14 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       w.rem += d;
       if (w.rem >= epi.rows.group) { w.rem -= epi.rows.group; ++w.quot; }
     };
-    // a row map whose group exceeds M sends row m to m + offset
     const bool plain_rows = epi.rows.group > M;
     if constexpr (KIND != kEpiResidual) {
-      // bf16 staging: row r (256 bytes) holds 16-byte chunk c at c ^ (r & 15)
+      // bf16 staging: row r (128 bytes) holds 16-byte chunk c at c ^ ((r >> 1) & 7)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = i * 32 + fr;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
@@ -330,79 +331,78 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
             u.x = pack_bf16x2(v[0], v[1]);
             u.y = pack_bf16x2(v[2], v[3]);
             const int c16 = 4 * j + q;
-            *reinterpret_cast<uint2*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4) + fk * 8) = u;
+            *reinterpret_cast<uint2*>(ep + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4) + fk * 8) = u;
           }
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's staging writes are done
-      const int c16 = lane & 15;
+      const int c16 = lane & 7;
       auto store_rows = [&](auto row_ptr) {
-        // all 32 row pieces come out of LDS first, so the stores issue back to back
-        u32x4 d[32];
+        u32x4 d[16];
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-          const int r = 4 * t + (lane >> 4);
-          d[t] = *reinterpret_cast<const u32x4*>(ep + r * 256 + ((c16 ^ (r & 15)) << 4));
+        for (int t = 0; t < 16; ++t) {
+          const int r = 8 * t + (lane >> 3);
+          d[t] = *reinterpret_cast<const u32x4*>(ep + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
         }
 #pragma unroll
-        for (int t = 0; t < 32; ++t) {
-          const int r = 4 * t + (lane >> 4);
+        for (int t = 0; t < 16; ++t) {
+          const int r = 8 * t + (lane >> 3);
           bf16* const dst = row_ptr(t);
           if (row_base + r < M) *reinterpret_cast<u32x4*>(dst + c16 * 8) = d[t];
         }
       };
       if (plain_rows) {
-        bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + (lane >> 4)) * ldc;
-        store_rows([&](int t) { return p0 + (long long)(4 * t) * ldc; });
+        bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + (lane >> 3)) * ldc;
+        store_rows([&](int t) { return p0 + (long long)(8 * t) * ldc; });
       } else {
-        RowWalk w = row_walk(lane >> 4);
-        store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 4); return q; });
+        RowWalk w = row_walk(lane >> 3);
+        store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 8); return q; });
       }
     } else {
-      // fp32 staging in two 64-row halves (row r: 512 bytes, 16-byte chunk c at
+      // fp32 staging in two 64-row halves (row r: 256 bytes, 16-byte chunk c at
       // c ^ (r & 15)); each half's residual rows are loaded first so their latency
       // overlaps the staging writes
-      const int ch = lane & 31;
+      const int ch = lane & 15;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        uint2 res[32];
+        uint2 res[16];
         auto load_rows = [&](auto row_ptr) {
 #pragma unroll
-          for (int t = 0; t < 32; ++t) {
-            const int r = 64 * h + 2 * t + (lane >> 5);
+          for (int t = 0; t < 16; ++t) {
+            const int r = 64 * h + 4 * t + (lane >> 4);
             const bf16* const src = row_ptr(t);
             res[t] = make_uint2(0u, 0u);
             if (row_base + r < M) res[t] = *reinterpret_cast<const uint2*>(src + ch * 4);
           }
         };
         if (plain_rows) {
-          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 5)) * ldc;
-          load_rows([&](int t) { return p0 + (long long)(2 * t) * ldc; });
+          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 4)) * ldc;
+          load_rows([&](int t) { return p0 + (long long)(4 * t) * ldc; });
         } else {
-          RowWalk w = row_walk(64 * h + (lane >> 5));
-          load_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 2); return q; });
+          RowWalk w = row_walk(64 * h + (lane >> 4));
+          load_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 4); return q; });
         }
 #pragma unroll
         for (int ii = 0; ii < 2; ++ii) {
           const int i = 2 * h + ii;
           const int r = ii * 32 + fr;
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
+          for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
               const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
                                            acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
               const int cw = 8 * j + 2 * q + fk;
-              *reinterpret_cast<float4*>(ep + r * 512 + ((cw ^ (r & 15)) << 4)) = v;
+              *reinterpret_cast<float4*>(ep + r * 256 + ((cw ^ (r & 15)) << 4)) = v;
             }
           __builtin_amdgcn_sched_barrier(0);
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);
         auto store_rows = [&](auto row_ptr) {
 #pragma unroll
-          for (int t = 0; t < 32; ++t) {
-            const int r = 2 * t + (lane >> 5);
-            const float4 f = *reinterpret_cast<const float4*>(ep + r * 512 + ((ch ^ (r & 15)) << 4));
+          for (int t = 0; t < 16; ++t) {
+            const int r = 4 * t + (lane >> 4);
+            const float4 f = *reinterpret_cast<const float4*>(ep + r * 256 + ((ch ^ (r & 15)) << 4));
             bf16* const dst = row_ptr(t);
             if (row_base + 64 * h + r < M) {
               const uint2 u = res[t];
@@ -413,11 +413,11 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           }
         };
         if (plain_rows) {
-          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 5)) * ldc;
-          store_rows([&](int t) { return p0 + (long long)(2 * t) * ldc; });
+          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 4)) * ldc;
+          store_rows([&](int t) { return p0 + (long long)(4 * t) * ldc; });
         } else {
-          RowWalk w = row_walk(64 * h + (lane >> 5));
-          store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 2); return q; });
+          RowWalk w = row_walk(64 * h + (lane >> 4));
+          store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 4); return q; });
         }
         __builtin_amdgcn_s_waitcnt(0xC07F);   // this half's reads are done before the next overwrites it
         __builtin_amdgcn_sched_barrier(0);
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     if (m >= M) continue;
     const long long row = epi.rows(m);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
