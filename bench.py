@@ -12,7 +12,9 @@ all 10 rounds), inputs resident in HBM.  Prints ONE JSON line:
   value       = candidate evaluations per second = N * R / plan time
   ms_per_step = milliseconds per plan step (graph replay)
   roofline    = the dense-GEMM kernel (the dominant kernel), useful FLOPs over
-                its HIP-event-timed launch durations, against bf16 dense MFMA peak
+                its HIP-event-timed launch durations, against bf16 dense MFMA peak;
+                next to it the part's own sustained register-only MFMA ceiling
+                (cem_mfma_ceiling), measured in the same run
   cpu_baseline= the oracle (NumPy float64) on the host cores, on a bounded
                 sample of candidates, extrapolated to the metric's unit
 """
@@ -224,6 +226,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timers", action="store_true")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the register-only MFMA ceiling measurement")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration only: run a plain device copy of this many bytes 3 times "
                          "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
@@ -342,13 +346,25 @@ def main() -> int:
         traffic = None
         if m.dtype == "bf16" and gemm_sources_sha256() == GEMM_COUNTERS["sources_sha256"]:
             traffic = GEMM_COUNTERS["bytes_per_launch"]
+        ceiling = None
+        if m.dtype == "bf16" and not args.no_ceiling:
+            # the part's own sustained MFMA ceiling, register-only: with changing operand
+            # bits it lowers its clock to stay within its power limit
+            rt, rmhz = _lib.mfma_ceiling(True, 40)
+            ct, cmhz = _lib.mfma_ceiling(False, 20)
+            ceiling = {"random_operands_tflops": round(rt, 1), "random_operands_mhz": round(rmhz),
+                       "constant_operands_tflops": round(ct, 1), "constant_operands_mhz": round(cmhz),
+                       "achieved_frac_of_random": round(achieved / rt, 4)}
+            eprint(f"[bench] MFMA ceiling: {rt:.0f} TFLOP/s at {rmhz:.0f} MHz (random operands), "
+                   f"{ct:.0f} TFLOP/s at {cmhz:.0f} MHz (constant operands)")
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "traffic_unit": "HBM-side bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                 "copy-calibrated)",
                 "kernel": "gemm_bf16_kernel" if m.dtype == "bf16" else "gemm_f32_kernel",
                 "launches": launches, "avg_launch_ms": round(gemm_ms / max(launches, 1), 4),
-                "gemm_share_of_step": round(gemm_ms / nt / eager_ms, 4)}
+                "gemm_share_of_step": round(gemm_ms / nt / eager_ms, 4),
+                "sustained_mfma_ceiling": ceiling}
         eprint(f"[bench] GEMMs: {launches} launches, {gemm_ms / nt:.2f} ms/step, "
                f"{achieved:.1f} TFLOP/s; eager step {eager_ms:.2f} ms")
 

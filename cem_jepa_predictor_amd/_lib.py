@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYP
 
 EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
            "cem_plan", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
-           "cem_sample", "topk_select", "cem_timer_enable", "cem_timer_read"]
+           "cem_sample", "topk_select", "cem_timer_enable", "cem_timer_read", "cem_mfma_ceiling"]
 
 
 class CemError(RuntimeError):
@@ -87,6 +87,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cem_timer_enable": [P, I32],
         "cem_timer_read": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)],
+        "cem_mfma_ceiling": [I32, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -327,3 +328,12 @@ def topk_select(energy, k, idx, stream=None):
     ptrs = _args((energy, "energy", _f32()), (idx, "idx", _i32(), (k,)))
     with _OnStream(stream) as st:
         _check(load().topk_select(ptrs[0], energy.numel(), k, ptrs[1], st))
+
+
+def mfma_ceiling(random_operands: bool = True, launches: int = 40):
+    """Sustained dense bf16 MFMA TFLOP/s and shader clock (MHz) of the current
+    device, register-only (cem_mfma_ceiling); synchronous."""
+    tf, mhz = ctypes.c_double(), ctypes.c_double()
+    _check(load().cem_mfma_ceiling(1 if random_operands else 0, int(launches), ctypes.byref(tf),
+                                   ctypes.byref(mhz)))
+    return tf.value, mhz.value

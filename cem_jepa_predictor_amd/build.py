@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 ARCH = "gfx950"
 
 SOURCES = ["sampler.hip", "embed.hip", "layernorm.hip", "gemm.hip", "attention.hip",
-           "energy.hip", "select_refit.hip", "model.hip", "abi.hip"]
+           "energy.hip", "select_refit.hip", "probe.hip", "model.hip", "abi.hip"]
 NO_CONTRACT = {"sampler.hip", "select_refit.hip"}
 # attention keeps its MFMA accumulators in VGPRs: its softmax rescales them with VALU ops
 EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}

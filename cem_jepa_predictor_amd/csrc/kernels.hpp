@@ -80,4 +80,10 @@ hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int
                                float* mu, float* sigma, hipStream_t stream);
 hipError_t select_init();
 
+// --- probe.hip -------------------------------------------------------------------
+// Sustained bf16 MFMA throughput (TFLOP/s) and shader clock (MHz) on the
+// current device over `launches` launches of a register-only MFMA loop
+// (first half untimed); synchronous.
+hipError_t mfma_ceiling(int random_operands, int launches, double* tflops, double* mhz);
+
 }  // namespace cem

@@ -112,6 +112,13 @@ def test_plan_calls_validate_null_model(lib):
     assert lib.cem_timer_enable(None, 1) == -1
 
 
+def test_mfma_ceiling_validates_before_launch(lib):
+    tf, mhz = ctypes.c_double(), ctypes.c_double()
+    assert lib.cem_mfma_ceiling(1, 1, ctypes.byref(tf), ctypes.byref(mhz)) == -1
+    assert lib.cem_mfma_ceiling(2, 10, ctypes.byref(tf), ctypes.byref(mhz)) == -1
+    assert lib.cem_mfma_ceiling(1, 10, None, ctypes.byref(mhz)) == -1
+
+
 def test_binding_rejects_bad_tensors_before_the_library():
     """dtype, shape, device and layout are checked in the binding, before any pointer
     crosses the ABI (a float64 goal read as float32 would give garbage energies)."""

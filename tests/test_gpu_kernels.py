@@ -159,3 +159,21 @@ def test_energy_l1_device_generated_inputs(gpu_lib):
     got, want = to_np(out), to_np(ref)
     log(f"  ours: nan {int(np.isnan(got).sum())}, untouched {int((got == -7.0).sum())}")
     np.testing.assert_allclose(got, want, rtol=2e-5, atol=0)
+
+
+def test_mfma_ceiling_probe_is_plausible(gpu_lib):
+    """The register-only MFMA probe cannot beat the part's published dense bf16
+    peak (2.5 PFLOP/s at 2.4 GHz, 256 CUs x 4096 FLOP/clk) and its clock reading
+    must be a real shader clock; with changing operand bits it runs no faster
+    than with constant ones (the part lowers its clock under power)."""
+    from cem_jepa_predictor_amd import _lib
+
+    ct, cmhz = _lib.mfma_ceiling(False, 6)
+    rt, rmhz = _lib.mfma_ceiling(True, 6)
+    log(f"mfma ceiling: constant {ct:.0f} TFLOP/s @ {cmhz:.0f} MHz, random {rt:.0f} TFLOP/s @ {rmhz:.0f} MHz")
+    for tf, mhz in ((ct, cmhz), (rt, rmhz)):
+        assert 300.0 < mhz < 2600.0
+        assert 100.0 < tf < 2600.0
+        # throughput and clock agree: 256 CUs x 4096 FLOP per clock at most
+        assert tf <= 256 * 4096 * mhz * 1e6 / 1e12 * 1.05
+    assert rt <= ct * 1.05
