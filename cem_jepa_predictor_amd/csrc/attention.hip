@@ -6,22 +6,31 @@
 // earlier blocks come from a KV cache instead of being recomputed.  Within a
 // block attention is bidirectional.  Softmax scale 1/sqrt(dh), fp32 softmax.
 //
-// bf16 kernel (dh = 64), one 256-thread workgroup per (candidate, head):
-//  * the keys/values of one frame block at a time (B keys, padded to a
-//    multiple of 32) are staged in dynamic LDS: K row-major with 16-byte
-//    chunks XOR-swizzled by key % 8, V transposed (Vt[dh][key], padded rows) so
-//    both MFMA operands are contiguous LDS reads.  74 KB at B = 258, so two
-//    workgroups share a CU and one's loads overlap the other's math;
-//  * each wave owns 16-row query tiles; per tile and staged block it computes
-//    all of S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (lane l holds the scores
-//    of query l % 16 in registers), takes the block's exact max, and keeps a
-//    running max / sum only across frame blocks (one rescale per block); then
-//    O^T += V^T P^T with P taken straight from registers: the MFMA sums over
-//    its 32 key slots, and the key each slot stands for is chosen so that the
-//    lane's own probabilities and the matching V^T entries line up (any
-//    consistent assignment of keys to slots gives the same sum);
+// bf16 kernels (dh = 64), one workgroup per (candidate, head).
+//
+// One frame block (the whole plan at horizon 1): 512 threads (8 waves), two
+// workgroups per CU, so each SIMD holds four waves.
+//  * K and V rows of the block (B keys, padded to a multiple of 32 with zero
+//    rows) go global -> LDS by buffer_load ... lds, both row-major with 16-byte
+//    chunks XOR-swizzled by key % 8: 74 KB.  Q fragments go straight to
+//    registers, one query tile ahead.
+//  * Each wave owns 16-row query tiles.  S^T = K Q^T with
+//    v_mfma_f32_16x16x32_bf16 (lane l holds the scores of query l % 16), in two
+//    key halves joined by one online-softmax rescale, so only half a row of
+//    scores is live in registers; exact max per half, one fma + exp2 per score.
+//  * O^T += V^T P^T with P taken straight from registers: the MFMA sums over
+//    its 32 key slots, and the key each slot stands for is chosen so the lane's
+//    own probabilities and the matching V^T entries line up.  V^T fragments
+//    come from the row-major V through gfx950's transposing LDS read
+//    (ds_read_b64_tr_b16): lane 16 g + 4 r + c reads 4 dh-values of key r,
+//    lane 16 g + i receives 4 keys of dh-row i.
 //  * HBM traffic per (candidate, head) is one read of Q, K, V and one write of
-//    O: the kernel is bandwidth-bound at the V-JEPA2-AC shape.
+//    O: at the V-JEPA2-AC shape the bound is HBM bandwidth plus the
+//    per-score exp2.
+//
+// Several frame blocks (KV cache, horizon > 1): 256 threads, K staged as above
+// and V transposed in LDS; an online softmax over 64-key groups.
+#include <type_traits>
 #include <utility>
 
 #include "kernels.hpp"
@@ -30,6 +39,9 @@ namespace cem {
 namespace {
 
 constexpr int kDh = 64;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t* lds_v4bf16_t;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
 constexpr int kMaxTilesPerWave = 5;  // 16-row query tiles per wave -> B <= 320
 constexpr int kMaxKeyTiles = 20;     // 16-key tiles per staged block -> B <= 320
 
@@ -51,137 +63,144 @@ __device__ __forceinline__ float wave_sum_q(float v) {
   return v;
 }
 
-// One frame block (every query sees exactly the B keys of its own block):
-// each query tile computes its full score block in registers, takes the exact
-// max, exponentiates once and finishes before the next tile.
+// One frame block (every query sees exactly the B keys of its own block).
+// 512 threads (8 waves) per (candidate, head); two workgroups share a CU, so
+// each SIMD holds four waves whose dependency chains (scores -> max -> exp ->
+// P V) hide one another.  K and V go global -> LDS by buffer_load ... lds
+// (rows past B read as zero).  Each wave owns the 16-query tiles w, w + 8, ...;
+// per tile the keys are taken in two halves with one online-softmax rescale
+// between them, which keeps the score registers to one half.
 // KT = ceil(B / 16): 16-key (and 16-query) tiles per block, fixed per model.
 template <int KT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_bf16_single_kernel(AttnArgs p) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_bf16_single_kernel(AttnArgs p) {
   constexpr int kKT2 = 2 * ((KT + 1) / 2);   // key tiles rounded up to MFMA k = 32 pairs
+  constexpr int kSG = kKT2 / 2;              // 32-key groups
+  constexpr int kSG0 = (kSG + 1) / 2;        // groups in the first half
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int B = p.B, kpad = kpad_of(B), vld = vt_ld_of(B);
+  const int B = p.B, kpad = kpad_of(B);
   uint8_t* k_lds = lds;
-  bf16* vt_lds = reinterpret_cast<bf16*>(lds + kpad * kDh * 2);
+  uint8_t* v_lds = lds + kpad * kDh * 2;   // row-major like K (read transposed)
 
   const int n = blockIdx.x / p.heads, h = blockIdx.x % p.heads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, ql = lane & 15;
+  const int vr4 = (lane >> 2) & 3, vc4 = lane & 3;   // transposing-read source slot
   const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
 
-  const bf16* kvb = static_cast<const bf16*>(p.kv[0]) + (long long)n * B * p.ldkv + h * kDh;
-  // Staging: every K and V load of this thread is issued before any LDS store, so
-  // the loads' latencies overlap instead of adding up.
-  // K: 8 lanes per 128-byte key row (coalesced), 16-byte swizzled LDS stores.
-  // V: a wave takes 16 keys x 4 chunks, so each transposed 2-byte store
-  // instruction writes 4 Vt rows x 32 contiguous bytes on distinct banks.
-  constexpr int kItems = (kpad_of(16 * KT) * 8 + 255) / 256;   // per thread, K and V each
-  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 kreg[kItems], vreg[kItems];
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = tid + 256 * it;
-    const int kr = item >> 3, ck = item & 7;
-    const int vr = (item & 15) + 16 * (item >> 7);
-    const int vc = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
-    if (item < kpad * 8) {
-      kreg[it] = *reinterpret_cast<const u32x4*>(kvb + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
-      vreg[it] = *reinterpret_cast<const u32x4*>(kvb + p.d + (long long)min(vr, B - 1) * p.ldkv + vc * 8);
+  // ---- K and V rows 0 .. kpad-1 of this (candidate, head) -> LDS, 8 rows (1 KB) per
+  // instruction; LDS row r holds 16-byte chunk c at c ^ (r & 7)
+  {
+    const bf16* kvb = static_cast<const bf16*>(p.kv[0]) + (long long)n * B * p.ldkv + h * kDh;
+    const int bytes = (B - 1) * p.ldkv * 2 + kDh * 2;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb), (short)0, bytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb + p.d), (short)0, bytes, 0x00020000);
+    const int rows8 = kpad >> 3, ninstr = 2 * rows8;
+    const int lrow = lane >> 3, lch = (lane & 7) ^ (lane >> 3);
+    for (int t = wave; t < ninstr; t += 8) {
+      const bool isv = t >= rows8;
+      const int r0 = 8 * (isv ? t - rows8 : t);
+      const int voff = (r0 + lrow) * p.ldkv * 2 + lch * 16;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_ptr_t)((isv ? v_lds : k_lds) + r0 * 128), 16, voff, 0, 0, 0);
     }
   }
-  // this wave's query fragments (tiles wave, wave + 4, ...), fetched with K and V
-  constexpr int kTilesPerWave = (KT + 3) / 4;
   const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
-  bf16x8_t qall[kTilesPerWave][2];
-#pragma unroll
-  for (int ti = 0; ti < kTilesPerWave; ++ti) {
-    const int qr = min((wave + 4 * ti) * 16 + ql, B - 1);
+  auto load_q = [&](int tile, bf16x8_t q[2]) {
+    const int qr = min(tile * 16 + ql, B - 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      qall[ti][s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
-  }
-  __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the first LDS store
-#pragma unroll
-  for (int it = 0; it < kItems; ++it) {
-    const int item = tid + 256 * it;
-    if (item < kpad * 8) {
-      const int kr = item >> 3, ck = item & 7;
-      *reinterpret_cast<u32x4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = kreg[it];
-      const int vr = (item & 15) + 16 * (item >> 7);
-      const int vc = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        vt_lds[(vc * 8 + e) * vld + vr] = static_cast<bf16>((vreg[it][e >> 1] >> (16 * (e & 1))) & 0xffffu);
-    }
-  }
+      q[s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+  };
+  bf16x8_t qf[2], qn[2];
+  load_q(wave, qf);
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's K/V rows and Q landed
   __syncthreads();
 
   bf16* obase = static_cast<bf16*>(p.o) + (long long)n * B * p.ldo + h * kDh;
-#pragma unroll
-  for (int ti = 0; ti < kTilesPerWave; ++ti) {
-    const int tile = wave + 4 * ti;
-    if (tile >= KT) break;
-    const bf16x8_t* const qf = qall[ti];
-    // S^T[key][q]: lane holds keys 16 kt + 4 g + r of query ql
-    f32x4_t st[kKT2];
-    float bmax = -INFINITY;
-#pragma unroll
-    for (int kt = 0; kt < kKT2; ++kt) {
-      st[kt] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (kt < KT) {
-        const int kr = kt * 16 + ql;
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-              k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // only the last key tile can hold padding keys; scores stay unscaled
-          // here (the scale is positive, so it commutes with the max)
-          const float v = (kt < KT - 1 || kt * 16 + 4 * g + r < B) ? acc[r] : -INFINITY;
-          st[kt][r] = v;
-          bmax = fmaxf(bmax, v);
-        }
-      }
-      // bound how many K fragments the scheduler keeps in flight (register pressure)
-      if ((kt & 3) == 3) __builtin_amdgcn_sched_barrier(0);
-    }
-    // p = exp((s - max) scale) = 2^(s sl2 - max sl2): one fma per score
-    const float nmax = -wave_max_q(bmax) * sl2;
-    float psum = 0.f;
-#pragma unroll
-    for (int kt = 0; kt < kKT2; ++kt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(st[kt][r], sl2, nmax));
-        st[kt][r] = e;
-        psum += e;
-      }
-    // O^T[dh][q] = V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
-    // 32 sg + 4 g + e (e < 4) or 32 sg + 16 + 4 g + (e - 4) (e >= 4)
+  for (int tile = wave; tile < KT; tile += 8) {
+    if (tile + 8 < KT) load_q(tile + 8, qn);
     f32x4_t oacc[4];
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.f;
+    // one half: key groups [SG_A, SG_B)
+    auto half = [&](auto sga, auto sgb) {
+      constexpr int SGA = decltype(sga)::value, SGB = decltype(sgb)::value;
+      constexpr int NT = 2 * (SGB - SGA);
+      // S^T[key][q]: lane holds keys 16 kt + 4 g + r of query ql
+      f32x4_t st[NT];
+      float bmax = -INFINITY;
 #pragma unroll
-    for (int sg = 0; sg < kKT2 / 2; ++sg) {
-      union { uint32_t u[4]; bf16x8_t v; } pf;
-      pf.u[0] = pack_bf16x2(st[2 * sg][0], st[2 * sg][1]);
-      pf.u[1] = pack_bf16x2(st[2 * sg][2], st[2 * sg][3]);
-      pf.u[2] = pack_bf16x2(st[2 * sg + 1][0], st[2 * sg + 1][1]);
-      pf.u[3] = pack_bf16x2(st[2 * sg + 1][2], st[2 * sg + 1][3]);
+      for (int i = 0; i < NT; ++i) {
+        const int kt = 2 * SGA + i;
+        st[i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (kt < KT) {
+          const int kr = kt * 16 + ql;
+          f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        const bf16* vrow = vt_lds + (dt * 16 + ql) * vld + 32 * sg + 4 * g;
-        union { uint2 u[2]; bf16x8_t v; } vf;
-        vf.u[0] = *reinterpret_cast<const uint2*>(vrow);
-        vf.u[1] = *reinterpret_cast<const uint2*>(vrow + 16);
-        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[dt], 0, 0, 0);
+          for (int s = 0; s < 2; ++s) {
+            const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+                k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[s], acc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            // only the last key tile can hold padding keys; scores stay unscaled
+            // here (the scale is positive, so it commutes with the max)
+            const float v = (kt < KT - 1 || kt * 16 + 4 * g + r < B) ? acc[r] : -INFINITY;
+            st[i][r] = v;
+            bmax = fmaxf(bmax, v);
+          }
+        }
+        // bound how many K fragments the scheduler keeps in flight (register pressure)
+        if ((i & 1) == 1) __builtin_amdgcn_sched_barrier(0);
       }
-    }
+      const float mnew = fmaxf(mrun, wave_max_q(bmax));   // finite: the first half has a valid key
+      const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);   // 0 on the first half
+      const float nmax = -mnew * sl2;
+      mrun = mnew;
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < NT; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(st[i][r], sl2, nmax));
+          st[i][r] = e;
+          psum += e;
+        }
+      lrun = fmaf(lrun, alpha, psum);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+      // O^T[dh][q] += V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
+      // 32 sg + 4 g + e (e < 4) or 32 sg + 16 + 4 g + (e - 4) (e >= 4)
+#pragma unroll
+      for (int j = 0; j < NT / 2; ++j) {
+        const int sg = SGA + j;
+        union { uint32_t u[4]; bf16x8_t v; } pf;
+        pf.u[0] = pack_bf16x2(st[2 * j][0], st[2 * j][1]);
+        pf.u[1] = pack_bf16x2(st[2 * j][2], st[2 * j][3]);
+        pf.u[2] = pack_bf16x2(st[2 * j + 1][0], st[2 * j + 1][1]);
+        pf.u[3] = pack_bf16x2(st[2 * j + 1][2], st[2 * j + 1][3]);
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt) {
+          // V^T fragment through transposing reads: lane 16 g + 4 r + c fetches
+          // V[key0 + r][16 dt + 4 c .. +3]; lane 16 g + i receives V[key0 + 0..3][16 dt + i]
+          const int row0 = 32 * sg + 4 * g + vr4, c16 = 2 * dt + (vc4 >> 1);
+          union { bf16x4_t hh[2]; bf16x8_t v; } vf;
+          vf.hh[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_v4bf16_t)(v_lds + row0 * 128 + ((c16 ^ (row0 & 7)) << 4) + (vc4 & 1) * 8));
+          const int row1 = row0 + 16;
+          vf.hh[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (lds_v4bf16_t)(v_lds + row1 * 128 + ((c16 ^ (row1 & 7)) << 4) + (vc4 & 1) * 8));
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[dt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    half(std::integral_constant<int, 0>{}, std::integral_constant<int, kSG0>{});
+    if constexpr (kSG0 < kSG) half(std::integral_constant<int, kSG0>{}, std::integral_constant<int, kSG>{});
     // lane holds O[q = 16 tile + ql][dh = 16 dt + 4 g + r]
-    const float inv = 1.0f / wave_sum_q(psum);
+    const float inv = 1.0f / wave_sum_q(lrun);
     const int q = tile * 16 + ql;
     if (q < B) {
 #pragma unroll
@@ -192,6 +211,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         *reinterpret_cast<uint2*>(obase + (long long)q * p.ldo + dt * 16 + 4 * g) = u;
       }
     }
+    qf[0] = qn[0]; qf[1] = qn[1];
   }
 }
 
@@ -397,7 +417,7 @@ hipError_t set_all(std::integer_sequence<int, KTs...>) {
 }
 template <int... KTs>
 void launch_kt(int kt, const AttnArgs& a, hipStream_t stream, std::integer_sequence<int, KTs...>) {
-  ((kt == KTs + 1 ? (attn_bf16_single_kernel<KTs + 1><<<a.n * a.heads, 256, lds_bytes_of(a.B), stream>>>(a), 0) : 0), ...);
+  ((kt == KTs + 1 ? (attn_bf16_single_kernel<KTs + 1><<<a.n * a.heads, 512, lds_bytes_of(a.B), stream>>>(a), 0) : 0), ...);
 }
 using KtRange = std::make_integer_sequence<int, kMaxKeyTiles>;
 

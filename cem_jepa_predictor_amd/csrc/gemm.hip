@@ -26,13 +26,19 @@
 //    kt+1 and frees slab kt-1's stage, so fragment reads never wait on it.
 //    Every MFMA, fragment read and load is placed explicitly (scheduling
 //    fences between single instructions).
-//  * Block -> tile map is XCD-aware: the dispatcher hands block b to XCD
-//    b % 8, so each XCD receives a contiguous range of logical tiles, ordered
-//    in groups of 8 row-tiles to share A and B panels in that XCD's L2.
+//  * Persistent: one workgroup per CU walks a sequence of tiles, and the
+//    operand ring runs on across tile boundaries, so the next tile's first
+//    slabs load while this tile's last slabs are computed and while its
+//    results are stored; no tile pays a prologue.
+//  * Tile order is XCD-aware: the dispatcher hands workgroup b to XCD b % 8;
+//    each XCD owns a contiguous range of logical tiles, ordered in groups of
+//    8 row-tiles to share A and B panels in that XCD's L2, dealt round-robin
+//    to its workgroups.
 //  * Ragged M / N: operand loads go through buffer resources bounded at the
 //    tile's last valid row (the hardware returns zero beyond it), stores are
 //    masked.  K must be a multiple of 32.
-//  * Results leave through LDS as full 128-byte row pieces (see the epilogue).
+//  * Results leave through the freed ring stage (4 KB a wave, 32 rows at a
+//    time) as full 128-byte row pieces.
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
 //    each carries only its own epilogue code.
 //
@@ -110,19 +116,9 @@ constexpr int GROUP_M = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ void tile_of_block(int b, int nb, int tiles_m, int tiles_n, int& tm,
-                                              int& tn) {
-  const int xcd = b & 7, slot = b >> 3;
-  const int base = nb >> 3, rem = nb & 7;
-  const int L = xcd * base + min(xcd, rem) + slot;
-  const int per_group = GROUP_M * tiles_n;
-  const int g = L / per_group;
-  const int first_m = g * GROUP_M;
-  const int gsize = min(tiles_m - first_m, GROUP_M);
-  const int in = L - g * per_group;
-  tm = first_m + in % gsize;
-  tn = in / gsize;
-}
+struct TileCoord {
+  int m0, n0, rows_a, rows_b;   // rows_a = rows_b = 0: no tile (loads read zeros)
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, int row0, int rows,
                                                             int ld, int k) {
@@ -140,12 +136,33 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STB];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
-  int tm, tn;
-  tile_of_block(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int rows_a = min(M - m0, BM), rows_b = min(N - n0, BN);
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
   const int KT = K / BK;
+
+  // This workgroup's tiles.  The dispatcher hands workgroup b to XCD b % 8; XCD x
+  // owns a contiguous range of logical tiles (groups of 8 row-tiles sharing A and
+  // B panels in that XCD's L2), dealt round-robin to its workgroups.
+  const int G = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int sx = (G >> 3) + (xcd < (G & 7) ? 1 : 0);
+  const int tbase = tiles >> 3, trem = tiles & 7;
+  const int tlo = xcd * tbase + min(xcd, trem), tcnt = tbase + (xcd < trem ? 1 : 0);
+  auto coord = [&](int i) {
+    TileCoord t{0, 0, 0, 0};
+    const int idx = slot + i * sx;
+    if (idx < tcnt) {
+      const int L = tlo + idx;
+      const int per_group = GROUP_M * tiles_n;
+      const int g = L / per_group;
+      const int first_m = g * GROUP_M;
+      const int gsize = min(tiles_m - first_m, GROUP_M);
+      const int in = L - g * per_group;
+      t.m0 = (first_m + in % gsize) * BM;
+      t.n0 = (in / gsize) * BN;
+      t.rows_a = min(M - t.m0, BM);
+      t.rows_b = min(N - t.n0, BN);
+    }
+    return t;
+  };
 
   // Operand slabs: global -> LDS by buffer_load ... lds (16 bytes a lane; one
   // instruction fills 1 KB of LDS, lane l at byte 16 l).  LDS row r (64 bytes,
@@ -156,17 +173,15 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
   const int voff_a = drow * lda * 2 + dchunk * 16, vstep_a = 16 * lda * 2;
   const int voff_b = drow * ldb * 2 + dchunk * 16, vstep_b = 16 * ldb * 2;
-  auto dma = [&](int kt, int stage) {
+  auto dma1 = [&](const TileCoord& t, int kt, int stage, int d) {
     const bool live = kt < KT;
-    const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, live ? rows_a : 0, lda, live ? kt * BK : 0);
-    const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, live ? rows_b : 0, ldb, live ? kt * BK : 0);
-    uint8_t* const sa = lds + stage * STB + wave * 32 * 64;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(sa + j * 1024), 16, voff_a + j * vstep_a, 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(sa + OPB + j * 1024), 16, voff_b + j * vstep_b, 0, 0, 0);
+    if (d < 2) {
+      const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, t.m0, live ? t.rows_a : 0, lda, live ? kt * BK : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + stage * STB + wave * 32 * 64 + d * 1024), 16, voff_a + d * vstep_a, 0, 0, 0);
+    } else {
+      const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, t.n0, live ? t.rows_b : 0, ldb, live ? kt * BK : 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + stage * STB + OPB + wave * 32 * 64 + (d - 2) * 1024), 16, voff_b + (d - 2) * vstep_b, 0, 0, 0);
+    }
   };
 
   // 8 waves in a 2 x 4 grid, wave (wm, wn) owns output rows 128 wm .. +127 and
@@ -179,25 +194,21 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int fsw = (fr >> 2) & 3;
   f32x16_t acc[4][2];
   bf16x8_t fa[2][4], fb[2][2];
-  auto frags = [&](int stage, int s, int buf) {
+  auto frag1 = [&](int stage, int s, int buf, int r) {
     const uint8_t* st = lds + stage * STB;
     const int pc = ((2 * s + fk) ^ fsw) << 4;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      fa[buf][i] = *reinterpret_cast<const bf16x8_t*>(st + arow + i * 2048 + pc);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      fb[buf][j] = *reinterpret_cast<const bf16x8_t*>(st + brow + j * 2048 + pc);
+    if (r < 4) fa[buf][r] = *reinterpret_cast<const bf16x8_t*>(st + arow + r * 2048 + pc);
+    else fb[buf][r - 4] = *reinterpret_cast<const bf16x8_t*>(st + brow + (r - 4) * 2048 + pc);
   };
   // The weight tile is the MFMA's first operand, so D[i][j] has j = output row
   // (lane % 32) and i = output column 8 (r / 4) + 4 (lane / 32) + r % 4.
-#define CEM_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
-#define CEM_FENCE __builtin_amdgcn_sched_barrier(0)
-
-  // accumulators start at the bias (lane quads are 4 consecutive output columns);
-  // the bias loads go first so their wait does not also wait for operand slabs
-  {
-    const int cb = n0 + wn * 64 + 4 * fk;
+  auto mfma1 = [&](int buf, int idx) {
+    const int i = idx >> 1, j = idx & 1;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
+  };
+  // accumulators start at the bias (lane quads are 4 consecutive output columns)
+  auto init_acc = [&](const TileCoord& t) {
+    const int cb = t.n0 + wn * 64 + 4 * fk;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -211,236 +222,212 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           acc[i][j][4 * q + 2] = bb.z; acc[i][j][4 * q + 3] = bb.w;
         }
       }
-  }
-  CEM_FENCE;
+  };
+#define CEM_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+#define F __builtin_amdgcn_sched_barrier(0)
+
+  TileCoord T = coord(0), Tn = coord(1);
+  if (T.rows_a == 0) return;   // no tile for this workgroup (uniform)
+  init_acc(T);
+  F;
 #pragma unroll
-  for (int s = 0; s <= LEAD; ++s) dma(s, s);
-  CEM_FENCE;
+  for (int s = 0; s <= LEAD; ++s)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dma1(T, s, s, d);
+  F;
   CEM_VMCNT(DMA_PER_WAVE * LEAD);   // slab 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
-  CEM_FENCE;
-  frags(0, 0, 0);
-  CEM_FENCE;
-  // Slab kt: MFMAs of k-substep 0 while substep 1's fragments are read; then
-  // wait for slab kt+1 and barrier (which also frees slab kt-1's stage for the
-  // load of slab kt+1+LEAD); MFMAs of substep 1 while slab kt+1's first
-  // fragments are read and this wave's share of slab kt+1+LEAD is requested.
-  // The pieces below are single instructions, placed one by one between
-  // scheduling fences.
-  auto mfma1 = [&](int buf, int idx) {
-    const int i = idx >> 1, j = idx & 1;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
-  };
-  auto frag1 = [&](int stage, int s, int buf, int r) {
-    const uint8_t* st = lds + stage * STB;
-    const int pc = ((2 * s + fk) ^ fsw) << 4;
-    if (r < 4) fa[buf][r] = *reinterpret_cast<const bf16x8_t*>(st + arow + r * 2048 + pc);
-    else fb[buf][r - 4] = *reinterpret_cast<const bf16x8_t*>(st + brow + (r - 4) * 2048 + pc);
-  };
-  auto dma1 = [&](int kt, int stage, int d) {
-    const bool live = kt < KT;
-    if (d < 2) {
-      const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, m0, live ? rows_a : 0, lda, live ? kt * BK : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + stage * STB + wave * 32 * 64 + d * 1024), 16, voff_a + d * vstep_a, 0, 0, 0);
-    } else {
-      const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, n0, live ? rows_b : 0, ldb, live ? kt * BK : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + stage * STB + OPB + wave * 32 * 64 + (d - 2) * 1024), 16, voff_b + (d - 2) * vstep_b, 0, 0, 0);
-    }
-  };
-#define F __builtin_amdgcn_sched_barrier(0)
+  F;
+#pragma unroll
+  for (int r = 0; r < 6; ++r) frag1(0, 0, 0, r);
+  F;
+  // The slab sequence runs on across tiles: slab KT + j is the next tile's slab j,
+  // so the next tile's first slabs load while this tile's last ones are computed
+  // and while its results are stored.
   int cur = 0, nxt = 1, fill = LEAD + 1;
-  for (int kt = 0; kt < KT; ++kt) {
-    // phase A: substep 0 MFMAs, substep 1 fragments read in between
-    mfma1(0, 0); F; frag1(cur, 1, 1, 0); F; frag1(cur, 1, 1, 1); F;
-    mfma1(0, 1); F; frag1(cur, 1, 1, 2); F; frag1(cur, 1, 1, 3); F;
-    mfma1(0, 2); F; frag1(cur, 1, 1, 4); F; frag1(cur, 1, 1, 5); F;
-    mfma1(0, 3); F;
-    mfma1(0, 4); F;
-    mfma1(0, 5); F;
-    mfma1(0, 6); F;
-    mfma1(0, 7); F;
-    // slab kt+1 landed everywhere; slab kt-1's stage is free for slab kt+1+LEAD
-    CEM_VMCNT(DMA_PER_WAVE * (LEAD - 1));
+  for (int ti = 1;; ++ti) {
+    int freed = 0;
+    for (int kt = 0; kt < KT; ++kt) {
+      // phase A: substep 0 MFMAs, substep 1 fragments read in between
+      mfma1(0, 0); F; frag1(cur, 1, 1, 0); F; frag1(cur, 1, 1, 1); F;
+      mfma1(0, 1); F; frag1(cur, 1, 1, 2); F; frag1(cur, 1, 1, 3); F;
+      mfma1(0, 2); F; frag1(cur, 1, 1, 4); F; frag1(cur, 1, 1, 5); F;
+      mfma1(0, 3); F;
+      mfma1(0, 4); F;
+      mfma1(0, 5); F;
+      mfma1(0, 6); F;
+      mfma1(0, 7); F;
+      // slab kt+1 landed everywhere; slab kt-1's stage is free for slab kt+1+LEAD
+      CEM_VMCNT(DMA_PER_WAVE * (LEAD - 1));
+      __builtin_amdgcn_s_barrier();
+      F;
+      // phase B: substep 1 MFMAs; the following slab's substep 0 fragments, then
+      // this wave's share of slab kt+1+LEAD (this tile's, or the next tile's)
+      const int ds = kt + 1 + LEAD;
+      const bool in_this = ds < KT;
+      const int dkt = in_this ? ds : ds - KT;
+      mfma1(1, 0); F; frag1(nxt, 0, 0, 0); F; frag1(nxt, 0, 0, 1); F;
+      mfma1(1, 1); F; frag1(nxt, 0, 0, 2); F; frag1(nxt, 0, 0, 3); F;
+      mfma1(1, 2); F; frag1(nxt, 0, 0, 4); F; frag1(nxt, 0, 0, 5); F;
+      mfma1(1, 3); F;
+      dma1(in_this ? T : Tn, dkt, fill, 0); F;
+      mfma1(1, 4); F;
+      dma1(in_this ? T : Tn, dkt, fill, 1); F;
+      mfma1(1, 5); F;
+      dma1(in_this ? T : Tn, dkt, fill, 2); F;
+      mfma1(1, 6); F;
+      dma1(in_this ? T : Tn, dkt, fill, 3); F;
+      mfma1(1, 7); F;
+      freed = cur;
+      cur = nxt; nxt = (nxt + 1 == NS) ? 0 : nxt + 1; fill = (fill + 1 == NS) ? 0 : fill + 1;
+    }
+    // every wave has consumed this tile's last slab: its stage is free for the epilogue
     __builtin_amdgcn_s_barrier();
     F;
-    // phase B: substep 1 MFMAs; slab kt+1's substep 0 fragments, then this wave's loads
-    mfma1(1, 0); F; frag1(nxt, 0, 0, 0); F; frag1(nxt, 0, 0, 1); F;
-    mfma1(1, 1); F; frag1(nxt, 0, 0, 2); F; frag1(nxt, 0, 0, 3); F;
-    mfma1(1, 2); F; frag1(nxt, 0, 0, 4); F; frag1(nxt, 0, 0, 5); F;
-    mfma1(1, 3); F;
-    dma1(kt + 1 + LEAD, fill, 0); F;
-    mfma1(1, 4); F;
-    dma1(kt + 1 + LEAD, fill, 1); F;
-    mfma1(1, 5); F;
-    dma1(kt + 1 + LEAD, fill, 2); F;
-    mfma1(1, 6); F;
-    dma1(kt + 1 + LEAD, fill, 3); F;
-    mfma1(1, 7); F;
-    cur = nxt; nxt = (nxt + 1 == NS) ? 0 : nxt + 1; fill = (fill + 1 == NS) ? 0 : fill + 1;
-  }
-#undef F
-  CEM_VMCNT(0);
-  __builtin_amdgcn_s_barrier();   // every wave is done with the operand stages
-  CEM_FENCE;
-#undef CEM_FENCE
-#undef CEM_VMCNT
 
-  const int ncol = n0 + wn * 64 + 4 * fk;
-  const bool to_c0 = n0 + BN <= epi.split, to_c1 = n0 >= epi.split;
-  bf16* const cbase = static_cast<bf16*>(to_c0 ? epi.c0 : epi.c1);
-  const int ldc = to_c0 ? epi.ld0 : epi.ld1;
-  const int cshift = to_c0 ? 0 : epi.split;
-  if ((to_c0 || to_c1) && n0 + BN <= N && (ldc & 7) == 0 && (cshift & 7) == 0 &&
-      epi.rows.group >= 8 && ((uintptr_t)cbase & 15) == 0) {
-    // Each wave stages its 128 x 64 result in its own part of the freed operand
-    // LDS, then writes whole 128-byte row pieces (16 bytes a lane, 8 rows per
-    // store instruction).
-    uint8_t* const ep = lds + wave * 16384;
-    bf16* const cwave = cbase + (n0 + wn * 64 - cshift);
-    const int row_base = m0 + wm * 128;
-    struct RowWalk {
-      long long quot;
-      int rem;
-    };
-    auto row_walk = [&](int r) {
-      const int m = row_base + r;
-      return RowWalk{(long long)(m / epi.rows.group), m % epi.rows.group};
-    };
-    auto row_of = [&](const RowWalk& w) { return w.quot * epi.rows.stride + epi.rows.offset + w.rem; };
-    auto row_step = [&](RowWalk& w, int d) {
-      w.rem += d;
-      if (w.rem >= epi.rows.group) { w.rem -= epi.rows.group; ++w.quot; }
-    };
-    const bool plain_rows = epi.rows.group > M;
-    if constexpr (KIND != kEpiResidual) {
-      // bf16 staging: row r (128 bytes) holds 16-byte chunk c at c ^ ((r >> 1) & 7)
+    const int ncol = T.n0 + wn * 64 + 4 * fk;
+    const bool to_c0 = T.n0 + BN <= epi.split, to_c1 = T.n0 >= epi.split;
+    bf16* const cbase = static_cast<bf16*>(to_c0 ? epi.c0 : epi.c1);
+    const int ldc = to_c0 ? epi.ld0 : epi.ld1;
+    const int cshift = to_c0 ? 0 : epi.split;
+    if ((to_c0 || to_c1) && T.n0 + BN <= N && (ldc & 7) == 0 && (cshift & 7) == 0 &&
+        epi.rows.group >= 8 && ((uintptr_t)cbase & 15) == 0) {
+      // Each wave stages its 128 x 64 result 32 rows at a time in its own 4 KB of
+      // the freed stage (row r: 128 bytes, 16-byte chunk c at c ^ ((r >> 1) & 7)),
+      // then writes whole 128-byte row pieces (8 rows per store instruction).
+      uint8_t* const ep = lds + freed * STB + wave * 4096;
+      bf16* const cwave = cbase + (T.n0 + wn * 64 - cshift);
+      const int row_base = T.m0 + wm * 128;
+      const bool plain_rows = epi.rows.group > M;
+      // destination row of local row 8 t + lane / 8 of each 32-row block, walked in
+      // steps of 8 (row map group >= 8)
+      long long quot = 0;
+      int rem = 0;
+      if (!plain_rows) {
+        const int m = row_base + (lane >> 3);
+        quot = m / epi.rows.group;
+        rem = m % epi.rows.group;
+      }
+      auto next_row = [&]() -> bf16* {
+        bf16* q = cwave + (quot * epi.rows.stride + epi.rows.offset + rem) * ldc;
+        rem += 8;
+        if (rem >= epi.rows.group) { rem -= epi.rows.group; ++quot; }
+        return q;
+      };
+      const int c16r = lane & 7;
+      if constexpr (KIND == kEpiResidual) {
+        // the residual rows, loaded two blocks ahead (16 bytes a lane, 8 rows per load)
+        u32x4 res[3][4];
+        auto load_res = [&](int i, u32x4 (&r)[4]) {
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int m = row_base + i * 32 + 8 * t + (lane >> 3);
+            const long long row = plain_rows ? (long long)epi.rows.offset + m : epi.rows(m);
+            r[t] = u32x4{0u, 0u, 0u, 0u};
+            if (m < M) r[t] = *reinterpret_cast<const u32x4*>(cwave + row * ldc + c16r * 8);
+          }
+        };
+        load_res(0, res[0]);
+        load_res(1, res[1]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (i + 2 < 4) load_res(i + 2, res[(i + 2) % 3]);
+          // residual rows into the staging slots
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int rr = 8 * t + (lane >> 3);
+            *reinterpret_cast<u32x4*>(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4)) = res[i % 3][t];
+          }
+          // add the accumulators in fp32 and round once, in place
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int c16 = 4 * j + q;
+              uint2* const slotp = reinterpret_cast<uint2*>(ep + fr * 128 + ((c16 ^ ((fr >> 1) & 7)) << 4) + fk * 8);
+              const uint2 u = *slotp;
+              uint2 o;
+              o.x = pack_bf16x2(__uint_as_float(u.x << 16) + acc[i][j][4 * q],
+                                __uint_as_float(u.x & 0xffff0000u) + acc[i][j][4 * q + 1]);
+              o.y = pack_bf16x2(__uint_as_float(u.y << 16) + acc[i][j][4 * q + 2],
+                                __uint_as_float(u.y & 0xffff0000u) + acc[i][j][4 * q + 3]);
+              *slotp = o;
+            }
+          u32x4 d[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int rr = 8 * t + (lane >> 3);
+            d[t] = *reinterpret_cast<const u32x4*>(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int m = row_base + i * 32 + 8 * t + (lane >> 3);
+            bf16* const dst = plain_rows ? cwave + ((long long)epi.rows.offset + m) * ldc : next_row();
+            if (m < M) *reinterpret_cast<u32x4*>(dst + c16r * 8) = d[t];
+          }
+          F;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                            acc[i][j][4 * q + 3]};
+              if constexpr (KIND == kEpiGelu) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] = gelu_bf16_path(v[e]);
+              }
+              uint2 u;
+              u.x = pack_bf16x2(v[0], v[1]);
+              u.y = pack_bf16x2(v[2], v[3]);
+              const int c16 = 4 * j + q;
+              *reinterpret_cast<uint2*>(ep + fr * 128 + ((c16 ^ ((fr >> 1) & 7)) << 4) + fk * 8) = u;
+            }
+          u32x4 d[4];
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int rr = 8 * t + (lane >> 3);
+            d[t] = *reinterpret_cast<const u32x4*>(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4));
+          }
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            const int m = row_base + i * 32 + 8 * t + (lane >> 3);
+            bf16* const dst = plain_rows ? cwave + ((long long)epi.rows.offset + m) * ldc : next_row();
+            if (m < M) *reinterpret_cast<u32x4*>(dst + c16r * 8) = d[t];
+          }
+          F;
+        }
+      }
+    } else {
+      Epilogue e_nb = epi;
+      e_nb.bias = nullptr;   // already in the accumulators
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = i * 32 + fr;
+        const int m = T.m0 + wm * 128 + i * 32 + fr;
+        if (m >= M) continue;
+        const long long row = epi.rows(m);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                           acc[i][j][4 * q + 3]};
-            if constexpr (KIND == kEpiGelu) {
-#pragma unroll
-              for (int e = 0; e < 4; ++e) v[e] = gelu_bf16_path(v[e]);
-            }
-            uint2 u;
-            u.x = pack_bf16x2(v[0], v[1]);
-            u.y = pack_bf16x2(v[2], v[3]);
-            const int c16 = 4 * j + q;
-            *reinterpret_cast<uint2*>(ep + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4) + fk * 8) = u;
+            epilogue_row4<bf16, KIND>(e_nb, N, row, ncol + j * 32 + 8 * q, v);
           }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // this wave's staging writes are done
-      const int c16 = lane & 7;
-      auto store_rows = [&](auto row_ptr) {
-        u32x4 d[16];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = 8 * t + (lane >> 3);
-          d[t] = *reinterpret_cast<const u32x4*>(ep + r * 128 + ((c16 ^ ((r >> 1) & 7)) << 4));
-        }
-#pragma unroll
-        for (int t = 0; t < 16; ++t) {
-          const int r = 8 * t + (lane >> 3);
-          bf16* const dst = row_ptr(t);
-          if (row_base + r < M) *reinterpret_cast<u32x4*>(dst + c16 * 8) = d[t];
-        }
-      };
-      if (plain_rows) {
-        bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + (lane >> 3)) * ldc;
-        store_rows([&](int t) { return p0 + (long long)(8 * t) * ldc; });
-      } else {
-        RowWalk w = row_walk(lane >> 3);
-        store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 8); return q; });
-      }
-    } else {
-      // fp32 staging in two 64-row halves (row r: 256 bytes, 16-byte chunk c at
-      // c ^ (r & 15)); each half's residual rows are loaded first so their latency
-      // overlaps the staging writes
-      const int ch = lane & 15;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        uint2 res[16];
-        auto load_rows = [&](auto row_ptr) {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int r = 64 * h + 4 * t + (lane >> 4);
-            const bf16* const src = row_ptr(t);
-            res[t] = make_uint2(0u, 0u);
-            if (row_base + r < M) res[t] = *reinterpret_cast<const uint2*>(src + ch * 4);
-          }
-        };
-        if (plain_rows) {
-          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 4)) * ldc;
-          load_rows([&](int t) { return p0 + (long long)(4 * t) * ldc; });
-        } else {
-          RowWalk w = row_walk(64 * h + (lane >> 4));
-          load_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 4); return q; });
-        }
-#pragma unroll
-        for (int ii = 0; ii < 2; ++ii) {
-          const int i = 2 * h + ii;
-          const int r = ii * 32 + fr;
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float4 v = make_float4(acc[i][j][4 * q], acc[i][j][4 * q + 1],
-                                           acc[i][j][4 * q + 2], acc[i][j][4 * q + 3]);
-              const int cw = 8 * j + 2 * q + fk;
-              *reinterpret_cast<float4*>(ep + r * 256 + ((cw ^ (r & 15)) << 4)) = v;
-            }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);
-        auto store_rows = [&](auto row_ptr) {
-#pragma unroll
-          for (int t = 0; t < 16; ++t) {
-            const int r = 4 * t + (lane >> 4);
-            const float4 f = *reinterpret_cast<const float4*>(ep + r * 256 + ((ch ^ (r & 15)) << 4));
-            bf16* const dst = row_ptr(t);
-            if (row_base + 64 * h + r < M) {
-              const uint2 u = res[t];
-              float v[4] = {__uint_as_float(u.x << 16) + f.x, __uint_as_float(u.x & 0xffff0000u) + f.y,
-                            __uint_as_float(u.y << 16) + f.z, __uint_as_float(u.y & 0xffff0000u) + f.w};
-              Store4<bf16>::store(dst + ch * 4, v);
-            }
-          }
-        };
-        if (plain_rows) {
-          bf16* const p0 = cwave + (long long)(epi.rows.offset + row_base + 64 * h + (lane >> 4)) * ldc;
-          store_rows([&](int t) { return p0 + (long long)(4 * t) * ldc; });
-        } else {
-          RowWalk w = row_walk(64 * h + (lane >> 4));
-          store_rows([&](int) { bf16* const q = cwave + row_of(w) * ldc; row_step(w, 4); return q; });
-        }
-        __builtin_amdgcn_s_waitcnt(0xC07F);   // this half's reads are done before the next overwrites it
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    return;
+    if (Tn.rows_a == 0) break;
+    T = Tn;
+    Tn = coord(ti + 1);
+    init_acc(T);
+    F;
   }
-  Epilogue e_nb = epi;
-  e_nb.bias = nullptr;   // already in the accumulators
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int m = m0 + wm * 128 + i * 32 + fr;
-    if (m >= M) continue;
-    const long long row = epi.rows(m);
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                      acc[i][j][4 * q + 3]};
-        epilogue_row4<bf16, KIND>(e_nb, N, row, ncol + j * 32 + 8 * q, v);
-      }
-  }
+  CEM_VMCNT(0);   // drain the dummy loads of the slabs past the last tile
+#undef F
+#undef CEM_VMCNT
 }
 
 // ------------------------------------------------------------------ fp32 kernel
@@ -489,21 +476,48 @@ int epi_kind(const Epilogue& e) { return e.residual ? kEpiResidual : (e.gelu ? k
 
 }  // namespace
 
-hipError_t gemm_init() { return hipSuccess; }
+namespace {
+constexpr int kMaxDevices = 64;
+int g_cus[kMaxDevices] = {};   // compute units per device, filled on first use
+
+// Compute units of the current device (the persistent grid is one workgroup per CU).
+hipError_t cu_count(int* cus) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices && g_cus[dev] > 0) {
+    *cus = g_cus[dev];
+    return hipSuccess;
+  }
+  e = hipDeviceGetAttribute(cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  if (dev >= 0 && dev < kMaxDevices) g_cus[dev] = *cus;
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t gemm_init() {
+  int cus = 0;
+  return cu_count(&cus);
+}
 
 hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N, int K,
                             const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  int cus = 0;
+  const hipError_t ce = cu_count(&cus);
+  if (ce != hipSuccess) return ce;
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int grid = tiles < cus ? tiles : cus;   // persistent: one workgroup per CU
   switch (epi_kind(epi)) {
     case kEpiGelu:
-      gemm_bf16_kernel<kEpiGelu><<<tiles, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      gemm_bf16_kernel<kEpiGelu><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
       break;
     case kEpiResidual:
-      gemm_bf16_kernel<kEpiResidual><<<tiles, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      gemm_bf16_kernel<kEpiResidual><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
       break;
     default:
-      gemm_bf16_kernel<kEpiPlain><<<tiles, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      gemm_bf16_kernel<kEpiPlain><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
   }
   return hipGetLastError();
 }

@@ -46,7 +46,7 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
                             int K, const Epilogue& epi, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N,
                            int K, const Epilogue& epi, hipStream_t stream);
-hipError_t gemm_init();   // one-time function attributes (LDS size)
+hipError_t gemm_init();   // caches the current device's CU count (persistent grid size)
 
 // --- attention.hip -------------------------------------------------------------
 // Queries: rows n*B + i of q (head h at columns h*dh); keys/values of frame
