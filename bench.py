@@ -40,8 +40,8 @@ MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (reference for fp32 models)
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
 # as null once those change.
 GEMM_COUNTERS = {
-    "sources_sha256": "f80d7b787efefaf30bd40a151d5a2160ef84b91a25fd835168b36f92723625dc",
-    "bytes_per_launch": 3463254216,
+    "sources_sha256": "25e86991c5ad91b40c4fccd45dc64ce17024760c1dc97cbcd5222c65a2b6cc81",
+    "bytes_per_launch": 3585808507,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 
