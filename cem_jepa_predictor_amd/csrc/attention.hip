@@ -28,8 +28,9 @@
 //    O: at the V-JEPA2-AC shape the bound is HBM bandwidth plus the
 //    per-score exp2.
 //
-// Several frame blocks (KV cache, horizon > 1): 256 threads, K staged as above
-// and V transposed in LDS; an online softmax over 64-key groups.
+// Several frame blocks (KV cache, horizon > 1): the same 512-thread structure
+// with the blocks streamed through LDS one at a time and, per query tile, the
+// online-softmax state carried across blocks in registers.
 #include <type_traits>
 #include <utility>
 
@@ -42,14 +43,11 @@ constexpr int kDh = 64;
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4_t* lds_v4bf16_t;
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-constexpr int kMaxTilesPerWave = 5;  // 16-row query tiles per wave -> B <= 320
-constexpr int kMaxKeyTiles = 20;     // 16-key tiles per staged block -> B <= 320
+constexpr int kMaxKeyTiles = 20;     // 16-key tiles per frame block -> B <= 320
 
 constexpr __host__ __device__ int kpad_of(int B) { return (B + 31) & ~31; }
-__host__ __device__ __forceinline__ int vt_ld_of(int B) { return kpad_of(B) + 8; }
-__host__ __device__ __forceinline__ int lds_bytes_of(int B) {
-  return kpad_of(B) * kDh * 2 + kDh * vt_ld_of(B) * 2;
-}
+// K and V of one frame block, row-major, padded to a multiple of 32 keys
+__host__ __device__ __forceinline__ int lds_bytes_of(int B) { return 2 * kpad_of(B) * kDh * 2; }
 
 __device__ __forceinline__ float wave_max_q(float v) {
   // lanes l, l^16, l^32, l^48 share query l % 16
@@ -215,151 +213,164 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   }
 }
 
-// Several frame blocks (KV cache): an online (running max / sum) softmax over
-// 64-key groups, rescaling the O accumulators whenever the max grows.
-__global__ __launch_bounds__(256) void attn_bf16_multi_kernel(AttnArgs p) {
+// Several frame blocks (KV cache): the single-block structure with the frame
+// blocks streamed through LDS one at a time.  Each wave keeps, for each of its
+// query tiles, a running max, a lane-partial sum and the O^T accumulators
+// across blocks (online softmax); keys of a block are taken in thirds so the
+// scores of one third and the state of three tiles fit 128 VGPRs.
+template <int KT>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) void attn_bf16_multi8_kernel(AttnArgs p) {
+  constexpr int kKT2 = 2 * ((KT + 1) / 2);   // key tiles per block, rounded up to pairs
+  constexpr int kSG = kKT2 / 2;              // 32-key groups per block
+  constexpr int kTPW = (KT + 7) / 8;         // query tiles per wave (at most)
+  constexpr int kP0 = (kSG + 2) / 3, kP1 = (kSG - kP0 + 1) / 2, kP2 = kSG - kP0 - kP1;
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int B = p.B, kpad = kpad_of(B), vld = vt_ld_of(B);
+  const int B = p.B, kpad = kpad_of(B);
   uint8_t* k_lds = lds;
-  bf16* vt_lds = reinterpret_cast<bf16*>(lds + kpad * kDh * 2);
+  uint8_t* v_lds = lds + kpad * kDh * 2;
 
   const int n = blockIdx.x / p.heads, h = blockIdx.x % p.heads;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q_tiles = (B + 15) / 16;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, ql = lane & 15;
-  const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
+  const int vr4 = (lane >> 2) & 3, vc4 = lane & 3;
+  const float sl2 = p.scale * 1.4426950408889634f;
 
   const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
-
-  // per query tile: Q fragments (B operand of S^T = K Q^T), running max / sum, O^T accumulators
-  bf16x8_t qf[kMaxTilesPerWave][2];
-  float mrun[kMaxTilesPerWave], lrun[kMaxTilesPerWave];
-  f32x4_t oacc[kMaxTilesPerWave][4];
-#pragma unroll
-  for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
-    const int tile = wave + 4 * ti;
+  auto load_q = [&](int tile, bf16x8_t q[2]) {
     const int qr = min(tile * 16 + ql, B - 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      qf[ti][s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+      q[s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+  };
+  auto keys = [&](auto ngc, int sg0, const bf16x8_t (&q)[2], f32x4_t (&oacc)[4], float& mrun, float& lrun) {
+    constexpr int NG = decltype(ngc)::value, NT = 2 * NG;
+    f32x4_t st[NT];
+    float bmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NT; ++i) {
+      const int kt = 2 * sg0 + i;
+      st[i] = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (kt < KT) {
+        const int kr = kt * 16 + ql;
+        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
+              k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, q[s], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float v = (kt < KT - 1 || kt * 16 + 4 * g + r < B) ? acc[r] : -INFINITY;
+          st[i][r] = v;
+          bmax = fmaxf(bmax, v);
+        }
+      }
+      if ((i & 1) == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    // every key group holds a valid key, so mnew is finite and alpha = 0 on the first pass
+    const float mnew = fmaxf(mrun, wave_max_q(bmax));
+    const float alpha = __builtin_amdgcn_exp2f((mrun - mnew) * sl2);
+    const float nmax = -mnew * sl2;
+    mrun = mnew;
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < NT; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(st[i][r], sl2, nmax));
+        st[i][r] = e;
+        psum += e;
+      }
+    lrun = fmaf(lrun, alpha, psum);
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+#pragma unroll
+    for (int j = 0; j < NG; ++j) {
+      const int sg = sg0 + j;
+      union { uint32_t u[4]; bf16x8_t v; } pf;
+      pf.u[0] = pack_bf16x2(st[2 * j][0], st[2 * j][1]);
+      pf.u[1] = pack_bf16x2(st[2 * j][2], st[2 * j][3]);
+      pf.u[2] = pack_bf16x2(st[2 * j + 1][0], st[2 * j + 1][1]);
+      pf.u[3] = pack_bf16x2(st[2 * j + 1][2], st[2 * j + 1][3]);
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const int row0 = 32 * sg + 4 * g + vr4, c16 = 2 * dt + (vc4 >> 1);
+        union { bf16x4_t hh[2]; bf16x8_t v; } vf;
+        vf.hh[0] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_v4bf16_t)(v_lds + row0 * 128 + ((c16 ^ (row0 & 7)) << 4) + (vc4 & 1) * 8));
+        const int row1 = row0 + 16;
+        vf.hh[1] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+            (lds_v4bf16_t)(v_lds + row1 * 128 + ((c16 ^ (row1 & 7)) << 4) + (vc4 & 1) * 8));
+        oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[dt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+
+  f32x4_t oacc[kTPW][4];
+  float mrun[kTPW], lrun[kTPW];
+#pragma unroll
+  for (int ti = 0; ti < kTPW; ++ti) {
     mrun[ti] = -INFINITY;
     lrun[ti] = 0.f;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
-
+  const int rows8 = kpad >> 3, ninstr = 2 * rows8;
+  const int lrow = lane >> 3, lch = (lane & 7) ^ (lane >> 3);
+  const int bytes = (B - 1) * p.ldkv * 2 + kDh * 2;
   for (int blk = 0; blk < p.nblk; ++blk) {
-    const bf16* kvb = static_cast<const bf16*>(p.kv[blk]) + (long long)n * B * p.ldkv + h * kDh;
-    // ---- K: 8 lanes per 128-byte key row (coalesced), 16-byte swizzled LDS stores
-    for (int item = tid; item < kpad * 8; item += 256) {
-      const int kr = item >> 3, ck = item & 7;
-      const uint4 v = *reinterpret_cast<const uint4*>(kvb + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
-      *reinterpret_cast<uint4*>(k_lds + kr * 128 + ((ck ^ (kr & 7)) << 4)) = v;
-    }
-    // ---- V: a wave takes 16 keys x 4 chunks, so each transposed 2-byte store
-    // instruction writes 4 Vt rows x 32 contiguous bytes on distinct banks
-    for (int item = tid; item < kpad * 8; item += 256) {
-      const int kr = (item & 15) + 16 * (item >> 7);
-      const int ck = ((item >> 4) & 3) + 4 * ((item >> 6) & 1);
-      const uint4 v = *reinterpret_cast<const uint4*>(kvb + p.d + (long long)min(kr, B - 1) * p.ldkv + ck * 8);
-      const bf16* ve = reinterpret_cast<const bf16*>(&v);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) vt_lds[(ck * 8 + e) * vld + kr] = ve[e];
-    }
-    __syncthreads();
-
-#pragma unroll
-    for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
-      const int tile = wave + 4 * ti;
-      if (tile >= q_tiles) break;
-      for (int g0 = 0; g0 < kpad; g0 += 64) {
-        const int nkt = min(4, (kpad - g0) >> 4);   // 4, or 2 in a trailing 32-key group
-        const int valid = B - g0;                   // keys >= valid are padding
-        // S^T[key][q]: lane holds keys g0 + 16 kt + 4 g + r of query ql
-        f32x4_t st[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) {
-          st[kt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          if (kt < nkt) {
-            const int kr = g0 + kt * 16 + ql;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-              const bf16x8_t kf = *reinterpret_cast<const bf16x8_t*>(
-                  k_lds + kr * 128 + (((4 * s + g) ^ (kr & 7)) << 4));
-              st[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ti][s], st[kt], 0, 0, 0);
-            }
-          }
-        }
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = kt * 16 + 4 * g + r;
-            const float v = (kt < nkt && key < valid) ? st[kt][r] * sl2 : -INFINITY;
-            st[kt][r] = v;
-            cmax = fmaxf(cmax, v);
-          }
-        cmax = wave_max_q(cmax);
-        const float mnew = fmaxf(mrun[ti], cmax);      // finite: every group has a valid key
-        const float alpha = exp2f(mrun[ti] - mnew);    // exp2(-inf) = 0 on the first group
-        mrun[ti] = mnew;
-        float psum = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float e = exp2f(st[kt][r] - mnew);
-            st[kt][r] = e;
-            psum += e;
-          }
-        lrun[ti] = lrun[ti] * alpha + psum;
-#pragma unroll
-        for (int dt = 0; dt < 4; ++dt) oacc[ti][dt] *= alpha;
-        // O^T[dh][q] += V^T[dh][key] P^T[key][q]; MFMA k-slot 8 g + e stands for key
-        // g0 + 32 sg + 4 g + e (e < 4) or g0 + 32 sg + 16 + 4 g + (e - 4) (e >= 4)
-#pragma unroll
-        for (int sg = 0; sg < 2; ++sg) {
-          if (2 * sg < nkt) {
-            union { uint32_t u[4]; bf16x8_t v; } pf;
-            pf.u[0] = pack_bf16x2(st[2 * sg][0], st[2 * sg][1]);
-            pf.u[1] = pack_bf16x2(st[2 * sg][2], st[2 * sg][3]);
-            pf.u[2] = pack_bf16x2(st[2 * sg + 1][0], st[2 * sg + 1][1]);
-            pf.u[3] = pack_bf16x2(st[2 * sg + 1][2], st[2 * sg + 1][3]);
-#pragma unroll
-            for (int dt = 0; dt < 4; ++dt) {
-              const bf16* vrow = vt_lds + (dt * 16 + ql) * vld + g0 + 32 * sg + 4 * g;
-              union { uint2 u[2]; bf16x8_t v; } vf;
-              vf.u[0] = *reinterpret_cast<const uint2*>(vrow);
-              vf.u[1] = *reinterpret_cast<const uint2*>(vrow + 16);
-              oacc[ti][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf.v, pf.v, oacc[ti][dt], 0, 0, 0);
-            }
-          }
-        }
+    if (blk > 0) __syncthreads();   // every wave is done with the previous block's K and V
+    {
+      const bf16* kvb = static_cast<const bf16*>(p.kv[blk]) + (long long)n * B * p.ldkv + h * kDh;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb), (short)0, bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb + p.d), (short)0, bytes, 0x00020000);
+      for (int t = wave; t < ninstr; t += 8) {
+        const bool isv = t >= rows8;
+        const int r0 = 8 * (isv ? t - rows8 : t);
+        const int voff = (r0 + lrow) * p.ldkv * 2 + lch * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_ptr_t)((isv ? v_lds : k_lds) + r0 * 128), 16, voff, 0, 0, 0);
       }
     }
+    bf16x8_t qf[2];
+    load_q(wave, qf);
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's K/V rows and Q landed
     __syncthreads();
+#pragma unroll
+    for (int ti = 0; ti < kTPW; ++ti) {
+      const int tile = wave + 8 * ti;
+      if (tile < KT) {
+        bf16x8_t qn[2];
+        if (ti + 1 < kTPW && tile + 8 < KT) load_q(tile + 8, qn);
+        keys(std::integral_constant<int, kP0>{}, 0, qf, oacc[ti], mrun[ti], lrun[ti]);
+        if constexpr (kP1 > 0) keys(std::integral_constant<int, kP1>{}, kP0, qf, oacc[ti], mrun[ti], lrun[ti]);
+        if constexpr (kP2 > 0) keys(std::integral_constant<int, kP2>{}, kP0 + kP1, qf, oacc[ti], mrun[ti], lrun[ti]);
+        if (ti + 1 < kTPW && tile + 8 < KT) { qf[0] = qn[0]; qf[1] = qn[1]; }
+      }
+    }
   }
-
-  // lane holds O[q = 16 tile + ql][dh = 16 dt + 4 g + r]
   bf16* obase = static_cast<bf16*>(p.o) + (long long)n * B * p.ldo + h * kDh;
 #pragma unroll
-  for (int ti = 0; ti < kMaxTilesPerWave; ++ti) {
-    const int tile = wave + 4 * ti;
-    if (tile >= q_tiles) break;
-    const float inv = 1.0f / wave_sum_q(lrun[ti]);
-    const int q = tile * 16 + ql;
-    if (q < B) {
+  for (int ti = 0; ti < kTPW; ++ti) {
+    const int tile = wave + 8 * ti;
+    if (tile < KT) {
+      const float inv = 1.0f / wave_sum_q(lrun[ti]);
+      const int q = tile * 16 + ql;
+      if (q < B) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) {
-        uint2 u;
-        u.x = pack_bf16x2(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv);
-        u.y = pack_bf16x2(oacc[ti][dt][2] * inv, oacc[ti][dt][3] * inv);
-        *reinterpret_cast<uint2*>(obase + (long long)q * p.ldo + dt * 16 + 4 * g) = u;
+        for (int dt = 0; dt < 4; ++dt) {
+          uint2 u;
+          u.x = pack_bf16x2(oacc[ti][dt][0] * inv, oacc[ti][dt][1] * inv);
+          u.y = pack_bf16x2(oacc[ti][dt][2] * inv, oacc[ti][dt][3] * inv);
+          *reinterpret_cast<uint2*>(obase + (long long)q * p.ldo + dt * 16 + 4 * g) = u;
+        }
       }
     }
   }
 }
+
 
 // fp32: one thread per query row, keys streamed from global memory with an
 // online softmax in fp32 (expf).  Used by fp32 models (small shapes).
@@ -400,7 +411,7 @@ __global__ __launch_bounds__(128) void attn_f32_kernel(AttnArgs p) {
 }  // namespace
 
 bool attention_bf16_supports(int dh, int B) {
-  return dh == kDh && B >= 1 && B <= 16 * 4 * kMaxTilesPerWave;
+  return dh == kDh && B >= 1 && B <= 16 * kMaxKeyTiles;
 }
 bool attention_f32_supports(int dh) { return dh == 16 || dh == 32 || dh == 64 || dh == 128; }
 
@@ -416,16 +427,30 @@ hipError_t set_all(std::integer_sequence<int, KTs...>) {
   return e;
 }
 template <int... KTs>
+void launch_multi_kt(int kt, const AttnArgs& a, hipStream_t stream, std::integer_sequence<int, KTs...>) {
+  ((kt == KTs + 1 ? (attn_bf16_multi8_kernel<KTs + 1><<<a.n * a.heads, 512, lds_bytes_of(a.B), stream>>>(a), 0) : 0), ...);
+}
+template <int KT>
+hipError_t set_multi_lds_attr() {
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_multi8_kernel<KT>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes_of(16 * KT));
+}
+template <int... KTs>
+hipError_t set_all_multi(std::integer_sequence<int, KTs...>) {
+  hipError_t e = hipSuccess;
+  ((e = (e == hipSuccess ? set_multi_lds_attr<KTs + 1>() : e)), ...);
+  return e;
+}
+template <int... KTs>
 void launch_kt(int kt, const AttnArgs& a, hipStream_t stream, std::integer_sequence<int, KTs...>) {
   ((kt == KTs + 1 ? (attn_bf16_single_kernel<KTs + 1><<<a.n * a.heads, 512, lds_bytes_of(a.B), stream>>>(a), 0) : 0), ...);
 }
 using KtRange = std::make_integer_sequence<int, kMaxKeyTiles>;
 
 hipError_t attention_init() {
-  const hipError_t e = set_all(KtRange{});
+  hipError_t e = set_all(KtRange{});
   if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&attn_bf16_multi_kernel),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, lds_bytes_of(16 * kMaxKeyTiles));
+  return set_all_multi(KtRange{});
 }
 
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
@@ -435,7 +460,7 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.nblk == 1)
     launch_kt(kt, a, stream, KtRange{});
   else
-    attn_bf16_multi_kernel<<<a.n * a.heads, 256, lds_bytes_of(a.B), stream>>>(a);
+    launch_multi_kt(kt, a, stream, KtRange{});
   return hipGetLastError();
 }
 
