@@ -504,6 +504,9 @@ hipError_t gemm_init() {
 hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N, int K,
                             const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  // the operand ring runs on into the next tile, whose slab j must be slab KT + j
+  // of the sequence: every tile needs at least LEAD + 1 slabs
+  if (K % BK != 0 || K < BK * (LEAD + 1)) return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = cu_count(&cus);
   if (ce != hipSuccess) return ce;
