@@ -63,6 +63,17 @@ def test_rollout_matches_oracle(gpu_lib, name, n):
     assert rel <= TOL[wl.model.dtype]
     ztol = 1e-4 if wl.model.dtype == "f32" else 5e-2
     assert np.abs(got - want).max() <= ztol * scale
+    if n >= 8:
+        # energy parity as a ranking: Pearson r of GPU vs oracle energies across the
+        # candidates, next to the ratio of the candidates' energy spread to the error.
+        # Gated at the page's 0.9999 for the fp32 model; for bf16 models under
+        # random-init weights the spread sits near bf16 resolution (logged only).
+        r = float(np.corrcoef(e_got, e_want)[0, 1])
+        err = float(np.sqrt(np.mean((e_got - e_want) ** 2)))
+        spread = float(np.std(e_want))
+        log(f"  Pearson r {r:.6f}; energy spread {spread:.3e} vs rms error {err:.3e} (ratio {spread / max(err, 1e-30):.1f})")
+        if wl.model.dtype == "f32":
+            assert r >= 0.9999
 
 
 def _lockstep(name, out, oracle_rows):
