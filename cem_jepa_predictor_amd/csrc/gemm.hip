@@ -38,7 +38,8 @@
 //    tile's last valid row (the hardware returns zero beyond it), stores are
 //    masked.  K must be a multiple of 32.
 //  * Results leave through the freed ring stage (4 KB a wave, 32 rows at a
-//    time) as full 128-byte row pieces.
+//    time) as full 128-byte row pieces, stored non-temporally (this kernel
+//    never reads them back).
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
 //    each carries only its own epilogue code.
 //
@@ -363,7 +364,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           for (int t = 0; t < 4; ++t) {
             const int m = row_base + i * 32 + 8 * t + (lane >> 3);
             bf16* const dst = plain_rows ? cwave + ((long long)epi.rows.offset + m) * ldc : next_row();
-            if (m < M) *reinterpret_cast<u32x4*>(dst + c16r * 8) = d[t];
+            if (m < M) __builtin_nontemporal_store(d[t], reinterpret_cast<u32x4*>(dst + c16r * 8));
           }
           F;
         }
@@ -396,7 +397,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           for (int t = 0; t < 4; ++t) {
             const int m = row_base + i * 32 + 8 * t + (lane >> 3);
             bf16* const dst = plain_rows ? cwave + ((long long)epi.rows.offset + m) * ldc : next_row();
-            if (m < M) *reinterpret_cast<u32x4*>(dst + c16r * 8) = d[t];
+            if (m < M) __builtin_nontemporal_store(d[t], reinterpret_cast<u32x4*>(dst + c16r * 8));
           }
           F;
         }
