@@ -18,14 +18,19 @@
 //    activation tile, so each lane's accumulator quads hold 4 consecutive
 //    output columns of one output row.
 //  * Operands: global -> LDS directly (buffer_load_dwordx4 ... lds, no VGPR
-//    staging) through a ring of 5 stages of BK = 32 (32 KB each: A and B slabs),
-//    three slabs in flight ahead of the one being read.  64-byte LDS rows hold
-//    their four 16-byte k-chunks at c ^ ((r >> 2) & 3), so fragment reads are
-//    free of bank conflicts; each lane loads the chunk that belongs at its slot.
-//  * One barrier per K-slab, in the middle of the slab: it publishes slab
-//    kt+1 and frees slab kt-1's stage, so fragment reads never wait on it.
-//    Every MFMA, fragment read and load is placed explicitly (scheduling
-//    fences between single instructions).
+//    staging) through a ring of five 32 KB entries, each holding one
+//    operand's 256 x 64 slab (BK = 64): a slab takes two entries, so two and
+//    a half slabs fit in LDS.  A K-slab of 64 makes every LDS row a whole
+//    128-byte row piece of the operand, and the LDS-DMA path moves whole
+//    128-byte pieces about 1.6x faster than the 64-byte halves of a 32-wide
+//    slab.  128-byte LDS rows hold their eight 16-byte k-chunks at
+//    c ^ ((r >> 1) & 7), so fragment reads are free of bank conflicts; each
+//    lane loads the chunk that belongs at its slot.
+//  * One barrier per K-slab, before its last substep (of four, 16 k-values
+//    each): it publishes slab s+1 and frees slab s's two entries, which take
+//    B of slab s+2 at once and A of slab s+2 one substep-0 later.  Every MFMA,
+//    fragment read and load is placed explicitly (scheduling fences between
+//    single instructions).
 //  * Persistent: one workgroup per CU walks a sequence of tiles, and the
 //    operand ring runs on across tile boundaries, so the next tile's first
 //    slabs load while this tile's last slabs are computed and while its
@@ -36,8 +41,9 @@
 //    to its workgroups.
 //  * Ragged M / N: operand loads go through buffer resources bounded at the
 //    tile's last valid row (the hardware returns zero beyond it), stores are
-//    masked.  K must be a multiple of 32.
-//  * Results leave through the freed ring stage (4 KB a wave, 32 rows at a
+//    masked.  K must be a multiple of 64.
+//  * Results leave through the ring entry that the tile's last slab frees
+//    and that the next load into it waits for (4 KB a wave, 32 rows at a
 //    time) as full 128-byte row pieces, stored non-temporally (this kernel
 //    never reads them back).
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
@@ -107,12 +113,9 @@ __device__ __forceinline__ void epilogue_row4(const Epilogue& e, int N, long lon
 }
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
-constexpr int BM = 256, BN = 256, BK = 32, NTHR = 512;
-constexpr int NS = 5;                       // LDS stages in the operand ring
-constexpr int LEAD = NS - 2;                // slabs in flight ahead of the one being read
-constexpr int OPB = BM * BK * 2;            // 16 KB: one operand slab (256 rows x 64 B)
-constexpr int STB = 2 * OPB;                // 32 KB: A slab + B slab
-constexpr int DMA_PER_WAVE = 4;             // 1 KB instructions per wave per slab (2 A + 2 B)
+constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
+constexpr int NE = 5;                       // entries in the operand ring
+constexpr int ENT = BM * BK * 2;            // 32 KB: one operand slab (256 rows x 128 B)
 constexpr int GROUP_M = 8;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
@@ -134,7 +137,7 @@ template <int KIND>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
                                                          const bf16* __restrict__ Bt, int ldb,
                                                          int M, int N, int K, Epilogue epi) {
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[NS * STB];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[NE * ENT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
@@ -166,40 +169,49 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   };
 
   // Operand slabs: global -> LDS by buffer_load ... lds (16 bytes a lane; one
-  // instruction fills 1 KB of LDS, lane l at byte 16 l).  LDS row r (64 bytes,
-  // 4 chunks of 8 k-values) holds logical chunk c at position c ^ ((r >> 2) & 3),
-  // so each lane loads the chunk that belongs at its slot.  Wave w, instruction
-  // j < 2: local rows 32 w + 16 j + lane / 4 of A, then the same rows of B.
-  const int drow = 32 * wave + (lane >> 2);
-  const int dchunk = (lane & 3) ^ ((lane >> 4) & 3);
-  const int voff_a = drow * lda * 2 + dchunk * 16, vstep_a = 16 * lda * 2;
-  const int voff_b = drow * ldb * 2 + dchunk * 16, vstep_b = 16 * ldb * 2;
-  auto dma1 = [&](const TileCoord& t, int kt, int stage, int d) {
-    const bool live = kt < KT;
-    if (d < 2) {
-      const __amdgpu_buffer_rsrc_t ra = slab_rsrc(A, t.m0, live ? t.rows_a : 0, lda, live ? kt * BK : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + stage * STB + wave * 32 * 64 + d * 1024), 16, voff_a + d * vstep_a, 0, 0, 0);
-    } else {
-      const __amdgpu_buffer_rsrc_t rb = slab_rsrc(Bt, t.n0, live ? t.rows_b : 0, ldb, live ? kt * BK : 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + stage * STB + OPB + wave * 32 * 64 + (d - 2) * 1024), 16, voff_b + (d - 2) * vstep_b, 0, 0, 0);
-    }
+  // instruction fills 1 KB of LDS, lane l at byte 16 l).  The ring holds one
+  // operand's 256 x 64 slab per 32 KB entry: A of sequence slab g in entry
+  // 2g mod 5, B in 2g + 1 mod 5.  LDS row r (128 bytes, 8 chunks of 8 k-values)
+  // holds logical chunk c at position c ^ ((r >> 1) & 7); each lane loads the
+  // chunk that belongs at its slot, so one instruction reads 8 whole 128-byte
+  // row pieces.  Wave w, instruction d: local rows 32 w + 8 d + lane / 8.
+  const int dlrow = 32 * wave + (lane >> 3);
+  const int dpos = lane & 7, dsw = (lane >> 4) & 3;
+  const int dc0 = dpos ^ dsw, dc1 = dpos ^ (dsw | 4);           // d even / odd
+  const int va0 = dlrow * lda * 2 + (dc0 << 4), va1 = dlrow * lda * 2 + (dc1 << 4);
+  const int vb0 = dlrow * ldb * 2 + (dc0 << 4), vb1 = dlrow * ldb * 2 + (dc1 << 4);
+  auto dma_a = [&](const TileCoord& t, int kt, int entry, int d) {
+    const int kb = kt * BK;
+    const __amdgpu_buffer_rsrc_t r = slab_rsrc(A, t.m0, t.rows_a, lda, t.rows_a ? kb : 0);
+    const int v = ((d & 1) ? va1 : va0) + d * 16 * lda;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds + entry * ENT + wave * 4096 + d * 1024), 16, v, 0, 0, 0);
+  };
+  auto dma_b = [&](const TileCoord& t, int kt, int entry, int d) {
+    const int kb = kt * BK;
+    const __amdgpu_buffer_rsrc_t r = slab_rsrc(Bt, t.n0, t.rows_b, ldb, t.rows_b ? kb : 0);
+    const int v = ((d & 1) ? vb1 : vb0) + d * 16 * ldb;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds + entry * ENT + wave * 4096 + d * 1024), 16, v, 0, 0, 0);
   };
 
   // 8 waves in a 2 x 4 grid, wave (wm, wn) owns output rows 128 wm .. +127 and
   // columns 64 wn .. +63: 4 x 2 tiles of v_mfma_f32_32x32x16_bf16.
-  // Fragments: lane reads local row (l % 32) of a 32-row tile, k chunk 2 s + l / 32.
+  // Fragments: lane reads local row (l % 32) of a 32-row tile, k chunk 2 s + l / 32
+  // of substep s (16 k-values each, four per slab).
   const int wm = wave >> 2, wn = wave & 3;
   const int fr = lane & 31, fk = lane >> 5;
-  const int arow = (wm * 128 + fr) * 64;
-  const int brow = OPB + (wn * 64 + fr) * 64;
-  const int fsw = (fr >> 2) & 3;
+  const int arow = (wm * 128 + fr) * 128;
+  const int brow = (wn * 64 + fr) * 128;
+  const int fsw = (fr >> 1) & 7;
   f32x16_t acc[4][2];
   bf16x8_t fa[2][4], fb[2][2];
-  auto frag1 = [&](int stage, int s, int buf, int r) {
-    const uint8_t* st = lds + stage * STB;
+  auto frag1 = [&](int ea, int s, int buf, int r) {
     const int pc = ((2 * s + fk) ^ fsw) << 4;
-    if (r < 4) fa[buf][r] = *reinterpret_cast<const bf16x8_t*>(st + arow + r * 2048 + pc);
-    else fb[buf][r - 4] = *reinterpret_cast<const bf16x8_t*>(st + brow + (r - 4) * 2048 + pc);
+    if (r < 4) {
+      fa[buf][r] = *reinterpret_cast<const bf16x8_t*>(lds + ea * ENT + arow + r * 4096 + pc);
+    } else {
+      const int eb = (ea + 1 == NE) ? 0 : ea + 1;
+      fb[buf][r - 4] = *reinterpret_cast<const bf16x8_t*>(lds + eb * ENT + brow + (r - 4) * 4096 + pc);
+    }
   };
   // The weight tile is the MFMA's first operand, so D[i][j] has j = output row
   // (lane % 32) and i = output column 8 (r / 4) + 4 (lane / 32) + r % 4.
@@ -224,67 +236,95 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
         }
       }
   };
-#define CEM_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | 0x0F70)
+#define CEM_WAIT(vm) __builtin_amdgcn_s_waitcnt(((vm) & 15) | (((vm) >> 4) << 14) | (0 << 8) | 0x0070)
 #define F __builtin_amdgcn_sched_barrier(0)
 
-  TileCoord T = coord(0), Tn = coord(1);
+  // tiles ahead: slab s + 2 is at most two tiles on (one-slab tiles)
+  TileCoord T = coord(0), T1 = coord(1), T2 = coord(2);
   if (T.rows_a == 0) return;   // no tile for this workgroup (uniform)
+  auto tile_at = [&](int off) -> TileCoord { return off == 0 ? T : (off == 1 ? T1 : T2); };
   init_acc(T);
   F;
+  // prologue: A and B of slabs 0 and 1 into entries 0..3
+  {
+    const int o1 = (KT == 1) ? 1 : 0, k1 = 1 - o1 * KT;
+    const TileCoord t1 = tile_at(o1);
 #pragma unroll
-  for (int s = 0; s <= LEAD; ++s)
+    for (int d = 0; d < 4; ++d) dma_a(T, 0, 0, d);
 #pragma unroll
-    for (int d = 0; d < 4; ++d) dma1(T, s, s, d);
+    for (int d = 0; d < 4; ++d) dma_b(T, 0, 1, d);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dma_a(t1, k1, 2, d);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) dma_b(t1, k1, 3, d);
+  }
   F;
-  CEM_VMCNT(DMA_PER_WAVE * LEAD);   // slab 0 landed (this wave's part)
+  CEM_WAIT(8);   // slab 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
   F;
 #pragma unroll
   for (int r = 0; r < 6; ++r) frag1(0, 0, 0, r);
   F;
-  // The slab sequence runs on across tiles: slab KT + j is the next tile's slab j,
-  // so the next tile's first slabs load while this tile's last ones are computed
-  // and while its results are stored.
-  int cur = 0, nxt = 1, fill = LEAD + 1;
-  for (int ti = 1;; ++ti) {
-    int freed = 0;
+  // The slab sequence runs on across tiles: slab KT + j is the next tile's slab j.
+  // Slab s: substep 0 loads A of slab s + 2 into the entry that slab s - 1's B
+  // left (after the epilogue when slab s - 1 ended a tile: the results are staged
+  // there); substeps 0..2 read their successor's fragments; one barrier (slab
+  // s + 1 landed everywhere, slab s's entries free); substep 3 reads slab s + 1's
+  // first fragments and loads B of slab s + 2 into slab s's A entry.
+  int ea = 0;                                   // entry of the current slab's A (B: ea + 1)
+  int toff = (KT == 1) ? 2 : (KT == 2 ? 1 : 0);  // slab s + 2: tile offset and k-slab
+  int tkt = 2 - toff * KT;
+  for (int ti = 0;; ++ti) {
+    int stage_ep = 0;
     for (int kt = 0; kt < KT; ++kt) {
-      // phase A: substep 0 MFMAs, substep 1 fragments read in between
-      mfma1(0, 0); F; frag1(cur, 1, 1, 0); F; frag1(cur, 1, 1, 1); F;
-      mfma1(0, 1); F; frag1(cur, 1, 1, 2); F; frag1(cur, 1, 1, 3); F;
-      mfma1(0, 2); F; frag1(cur, 1, 1, 4); F; frag1(cur, 1, 1, 5); F;
+      const int eb = (ea + 1 == NE) ? 0 : ea + 1;
+      const int ea_n = (eb + 1 == NE) ? 0 : eb + 1;
+      const int ea_p = (ea == 0) ? NE - 1 : ea - 1;   // slab s - 1's B entry
+      const TileCoord Tt = tile_at(toff);
+      // substep 0
+      mfma1(0, 0); F; frag1(ea, 1, 1, 0); F; frag1(ea, 1, 1, 1); F;
+      mfma1(0, 1); F; frag1(ea, 1, 1, 2); F; frag1(ea, 1, 1, 3); F;
+      mfma1(0, 2); F; frag1(ea, 1, 1, 4); F; frag1(ea, 1, 1, 5); F;
       mfma1(0, 3); F;
+      dma_a(Tt, tkt, ea_p, 0); F;
       mfma1(0, 4); F;
+      dma_a(Tt, tkt, ea_p, 1); F;
       mfma1(0, 5); F;
+      dma_a(Tt, tkt, ea_p, 2); F;
       mfma1(0, 6); F;
+      dma_a(Tt, tkt, ea_p, 3); F;
       mfma1(0, 7); F;
-      // slab kt+1 landed everywhere; slab kt-1's stage is free for slab kt+1+LEAD
-      CEM_VMCNT(DMA_PER_WAVE * (LEAD - 1));
+      // substep 1
+      mfma1(1, 0); F; frag1(ea, 2, 0, 0); F; frag1(ea, 2, 0, 1); F;
+      mfma1(1, 1); F; frag1(ea, 2, 0, 2); F; frag1(ea, 2, 0, 3); F;
+      mfma1(1, 2); F; frag1(ea, 2, 0, 4); F; frag1(ea, 2, 0, 5); F;
+      mfma1(1, 3); F; mfma1(1, 4); F; mfma1(1, 5); F; mfma1(1, 6); F; mfma1(1, 7); F;
+      // substep 2
+      mfma1(0, 0); F; frag1(ea, 3, 1, 0); F; frag1(ea, 3, 1, 1); F;
+      mfma1(0, 1); F; frag1(ea, 3, 1, 2); F; frag1(ea, 3, 1, 3); F;
+      mfma1(0, 2); F; frag1(ea, 3, 1, 4); F; frag1(ea, 3, 1, 5); F;
+      mfma1(0, 3); F; mfma1(0, 4); F; mfma1(0, 5); F; mfma1(0, 6); F; mfma1(0, 7); F;
+      // slab s + 1 landed (every load but the last 4: A of slab s + 2), own reads done
+      CEM_WAIT(4);
       __builtin_amdgcn_s_barrier();
       F;
-      // phase B: substep 1 MFMAs; the following slab's substep 0 fragments, then
-      // this wave's share of slab kt+1+LEAD (this tile's, or the next tile's)
-      const int ds = kt + 1 + LEAD;
-      const bool in_this = ds < KT;
-      const int dkt = in_this ? ds : ds - KT;
-      mfma1(1, 0); F; frag1(nxt, 0, 0, 0); F; frag1(nxt, 0, 0, 1); F;
-      mfma1(1, 1); F; frag1(nxt, 0, 0, 2); F; frag1(nxt, 0, 0, 3); F;
-      mfma1(1, 2); F; frag1(nxt, 0, 0, 4); F; frag1(nxt, 0, 0, 5); F;
+      // substep 3
+      mfma1(1, 0); F; frag1(ea_n, 0, 0, 0); F; frag1(ea_n, 0, 0, 1); F;
+      mfma1(1, 1); F; frag1(ea_n, 0, 0, 2); F; frag1(ea_n, 0, 0, 3); F;
+      mfma1(1, 2); F; frag1(ea_n, 0, 0, 4); F; frag1(ea_n, 0, 0, 5); F;
       mfma1(1, 3); F;
-      dma1(in_this ? T : Tn, dkt, fill, 0); F;
+      dma_b(Tt, tkt, ea, 0); F;
       mfma1(1, 4); F;
-      dma1(in_this ? T : Tn, dkt, fill, 1); F;
+      dma_b(Tt, tkt, ea, 1); F;
       mfma1(1, 5); F;
-      dma1(in_this ? T : Tn, dkt, fill, 2); F;
+      dma_b(Tt, tkt, ea, 2); F;
       mfma1(1, 6); F;
-      dma1(in_this ? T : Tn, dkt, fill, 3); F;
+      dma_b(Tt, tkt, ea, 3); F;
       mfma1(1, 7); F;
-      freed = cur;
-      cur = nxt; nxt = (nxt + 1 == NS) ? 0 : nxt + 1; fill = (fill + 1 == NS) ? 0 : fill + 1;
+      if (++tkt == KT) { tkt = 0; ++toff; }
+      stage_ep = eb;
+      ea = ea_n;
     }
-    // every wave has consumed this tile's last slab: its stage is free for the epilogue
-    __builtin_amdgcn_s_barrier();
-    F;
 
     const int ncol = T.n0 + wn * 64 + 4 * fk;
     const bool to_c0 = T.n0 + BN <= epi.split, to_c1 = T.n0 >= epi.split;
@@ -294,9 +334,9 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     if ((to_c0 || to_c1) && T.n0 + BN <= N && (ldc & 7) == 0 && (cshift & 7) == 0 &&
         epi.rows.group >= 8 && ((uintptr_t)cbase & 15) == 0) {
       // Each wave stages its 128 x 64 result 32 rows at a time in its own 4 KB of
-      // the freed stage (row r: 128 bytes, 16-byte chunk c at c ^ ((r >> 1) & 7)),
+      // the free ring entry (row r: 128 bytes, 16-byte chunk c at c ^ ((r >> 1) & 7)),
       // then writes whole 128-byte row pieces (8 rows per store instruction).
-      uint8_t* const ep = lds + freed * STB + wave * 4096;
+      uint8_t* const ep = lds + stage_ep * ENT + wave * 4096;
       bf16* const cwave = cbase + (T.n0 + wn * 64 - cshift);
       const int row_base = T.m0 + wm * 128;
       const bool plain_rows = epi.rows.group > M;
@@ -420,15 +460,21 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           }
       }
     }
-    if (Tn.rows_a == 0) break;
-    T = Tn;
-    Tn = coord(ti + 1);
+    // every wave has read its staged rows back: entry stage_ep takes the pending A load
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    F;
+    if (T1.rows_a == 0) break;
+    T = T1;
+    T1 = T2;
+    T2 = coord(ti + 3);
+    --toff;
     init_acc(T);
     F;
   }
-  CEM_VMCNT(0);   // drain the dummy loads of the slabs past the last tile
+  CEM_WAIT(0);   // drain the dummy loads of the slabs past the last tile
 #undef F
-#undef CEM_VMCNT
+#undef CEM_WAIT
 }
 
 // ------------------------------------------------------------------ fp32 kernel
@@ -505,9 +551,7 @@ hipError_t gemm_init() {
 hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N, int K,
                             const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  // the operand ring runs on into the next tile, whose slab j must be slab KT + j
-  // of the sequence: every tile needs at least LEAD + 1 slabs
-  if (K % BK != 0 || K < BK * (LEAD + 1)) return hipErrorInvalidValue;
+  if (K <= 0 || K % BK != 0) return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = cu_count(&cus);
   if (ce != hipSuccess) return ce;

@@ -41,7 +41,7 @@ hipError_t launch_layernorm(const T* x, int rows, int d, RowMap in_rows, const f
 bool layernorm_supports(int d);
 
 // --- gemm.hip ----------------------------------------------------------------
-// out = epilogue(A[M, K] @ Bt[N, K]^T); N % 4 == 0; bf16 (MFMA): K % 32 == 0 and K >= 128
+// out = epilogue(A[M, K] @ Bt[N, K]^T); N % 4 == 0; bf16 (MFMA): K % 64 == 0
 // (hipErrorInvalidValue otherwise); fp32: K % 16 == 0.
 hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N,
                             int K, const Epilogue& epi, hipStream_t stream);

@@ -89,8 +89,6 @@ Status validate_desc(const cem_model_desc& d) {
   if (d.action_dim < 1 || d.action_dim > 32 || d.state_dim < 1 || d.state_dim > 32)
     return bad(CEM_E_SHAPE, "action_dim and state_dim must be in [1, 32]");
   if (d.max_horizon < 1 || d.max_horizon > kMaxBlocks) return bad(CEM_E_SHAPE, "max_horizon must be in [1, 8]");
-  if (d.dtype == CEM_BF16 && (d.d_mlp < 128 || d.enc_dim < 128))
-    return bad(CEM_E_SHAPE, "bf16 models need d_mlp >= 128 and enc_dim >= 128 (GEMM K >= 128)");
   if (d.max_horizon > 1 && d.state_dim != d.action_dim)
     return bad(CEM_E_SHAPE, "horizon > 1 advances the state by the action: state_dim must equal action_dim");
   if (d.max_samples < 1 || d.max_samples > kMaxSelect) return bad(CEM_E_SHAPE, "max_samples must be in [1, 16384]");

@@ -94,9 +94,10 @@ WORKLOADS: Dict[str, Workload] = {
     # Small bf16 case with a 3-step autoregressive rollout (KV cache).
     "small": Workload("small", ModelConfig("small", 6, 512, 8, 2048, 64, 512, "bf16", 3),
                       PlanConfig(256, 32, 5, 3)),
-    # Small bf16 case with odd K-slab counts (d_mlp 320, enc_dim 192) and ragged
-    # or split-straddling output tiles in every projection.
-    "oddk": Workload("oddk", ModelConfig("oddk", 2, 128, 2, 320, 16, 192, "bf16", 2),
+    # Small bf16 case with odd and single K-slab counts (64-wide slabs: d_mlp 320
+    # -> 5, d_model 128 -> 2, enc_dim 64 -> 1) and ragged or split-straddling
+    # output tiles in every projection.
+    "oddk": Workload("oddk", ModelConfig("oddk", 2, 128, 2, 320, 16, 64, "bf16", 2),
                      PlanConfig(16, 4, 2, 2)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),

@@ -65,19 +65,17 @@ def test_model_desc_validation(lib, field, value, status):
     assert lib.cem_last_error().decode() != ""
 
 
-def test_bf16_gemm_contraction_floor(lib):
-    """The bf16 GEMM's operand ring needs at least 4 K-slabs of 32 per tile, so bf16
-    models with a 64-wide MLP or encoder are refused at creation."""
+def test_bf16_gemm_takes_one_slab_contractions(lib):
+    """The bf16 GEMM's operand ring runs across tiles for any number of 64-wide
+    K-slabs, so bf16 models with a 64-wide MLP or encoder are accepted."""
     m = inputs.WORKLOADS["small"].model
     n = ctypes.c_size_t(0)
     for field in ("d_mlp", "enc_dim"):
         desc = _lib.model_desc(m, 8)
         setattr(desc, field, 64)
+        assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == 0
+        setattr(desc, field, 96)   # not a whole number of slabs
         assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == -2
-        assert "K >= 128" in lib.cem_last_error().decode()
-    desc = _lib.model_desc(inputs.WORKLOADS["tiny"].model, 8)   # fp32 models keep the 64 floor
-    desc.d_mlp = 64
-    assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == 0
 
 
 def test_bf16_attention_shape_limits(lib):
