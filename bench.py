@@ -40,8 +40,8 @@ MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (reference for fp32 models)
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
 # as null once those change.
 GEMM_COUNTERS = {
-    "sources_sha256": "4dc9f170e25967fffe050c6f10d2127c53aeb9ee014305bbdb36026840762d99",
-    "bytes_per_launch": 3587004790,
+    "sources_sha256": "bf2bed3cc33799d4f9bc42371741cc8c3276992dd14c7e25806dabc387f3cf28",
+    "bytes_per_launch": 3637994561,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 
