@@ -17,6 +17,11 @@ all 10 rounds), inputs resident in HBM.  Prints ONE JSON line:
                 (cem_mfma_ceiling), measured in the same run
   cpu_baseline= the oracle (NumPy float64) on the host cores, on a bounded
                 sample of candidates, extrapolated to the metric's unit
+
+--rounds R and --warm-start time the receding-horizon variant of section 06 B
+("Warm-started CEM"): every timed plan starts from cem_warm_start of the
+previous plan's final Gaussian (one step earlier, fresh last step, widths kept
+down to --sigma-floor) instead of the fresh Gaussian, with R rounds.
 """
 from __future__ import annotations
 
@@ -223,6 +228,11 @@ def main() -> int:
                     help="eager steps with the library's GEMM timers (roofline.achieved)")
     ap.add_argument("--workload", default="vjepa2ac")
     ap.add_argument("--samples", type=int, default=0, help="override N (sweep); K = N / 10")
+    ap.add_argument("--rounds", type=int, default=0, help="override R (rounds per plan)")
+    ap.add_argument("--warm-start", action="store_true",
+                    help="each plan starts from cem_warm_start of the previous one")
+    ap.add_argument("--sigma-floor", type=float, default=0.0,
+                    help="with --warm-start: carried widths are kept down to this value")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timers", action="store_true")
@@ -272,6 +282,10 @@ def main() -> int:
         wl = inputs.sweep_workload(args.samples)
     else:
         wl = inputs.WORKLOADS[args.workload]
+    if args.rounds:
+        import dataclasses
+
+        wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, rounds=args.rounds))
     m, pc = wl.model, wl.plan
     N, K, R, H, A = pc.n_samples, pc.n_elites, pc.rounds, pc.horizon, m.action_dim
     eprint(f"[bench] workload {wl.name}: N={N} K={K} R={R} H={H} L={m.layers} d={m.d_model} "
@@ -295,8 +309,11 @@ def main() -> int:
     stream = torch.cuda.current_stream()
 
     def step(i: int, use_graph: bool = True):
-        mu.copy_(mu0)
-        sg.copy_(sg0)
+        if args.warm_start:
+            _lib.warm_start(mu, sg, pc.mu0, pc.sigma0, args.sigma_floor, mu, sg, stream=stream)
+        else:
+            mu.copy_(mu0)
+            sg.copy_(sg0)
         model.plan(zo, zg, st, mu, sg, action, best, n_samples=N, n_elites=K, rounds=R, horizon=H,
                    seed=pc.seed, plan_id=i, clamp_lo=pc.clamp_lo, clamp_hi=pc.clamp_hi,
                    use_graph=use_graph, stream=stream)
@@ -383,6 +400,7 @@ def main() -> int:
         "data": "synthetic: random-init weights N(0,0.02) (seed 0), N(0,1) embeddings (seed 1), "
                 "CEM seed 2",
         "config": {"workload": wl.name, "n_samples": N, "n_elites": K, "rounds": R, "horizon": H,
+                   "warm_start": bool(args.warm_start),
                    "layers": m.layers, "d_model": m.d_model, "heads": m.heads, "d_mlp": m.d_mlp,
                    "patches": m.patches, "enc_dim": m.enc_dim, "graph_replay": True,
                    "eager_ms_per_step": round(eager_ms, 3) if eager_ms else None},

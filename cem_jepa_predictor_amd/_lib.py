@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYP
 
 EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
            "cem_plan", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
-           "cem_sample", "topk_select", "cem_timer_enable", "cem_timer_read", "cem_mfma_ceiling"]
+           "cem_sample", "topk_select", "cem_warm_start", "cem_timer_enable", "cem_timer_read",
+           "cem_mfma_ceiling"]
 
 
 class CemError(RuntimeError):
@@ -84,6 +85,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "elite_refit": [P, P, I32, I32, I32, I32, P, P, P, P],
         "cem_sample": [P, P, I32, I32, I32, U64, U32, U32, F32, F32, P, P, P],
         "topk_select": [P, I32, I32, P, P],
+        "cem_warm_start": [P, P, I32, I32, F32, F32, F32, P, P, P],
         "cem_timer_enable": [P, I32],
         "cem_timer_read": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)],
@@ -328,6 +330,20 @@ def topk_select(energy, k, idx, stream=None):
     ptrs = _args((energy, "energy", _f32()), (idx, "idx", _i32(), (k,)))
     with _OnStream(stream) as st:
         _check(load().topk_select(ptrs[0], energy.numel(), k, ptrs[1], st))
+
+
+def warm_start(mu_prev, sigma_prev, mu_fill, sigma_fill, sigma_floor, mu_next, sigma_next,
+               stream=None):
+    """Seeds the next control step's Gaussian from a plan's final one
+    (cem_warm_start); outputs may be the inputs."""
+    if mu_prev.dim() != 2:
+        raise ValueError(f"mu_prev: expected [h, a], got {tuple(mu_prev.shape)}")
+    h, a = mu_prev.shape
+    ptrs = _args((mu_prev, "mu_prev", _f32()), (sigma_prev, "sigma_prev", _f32(), (h, a)),
+                 (mu_next, "mu_next", _f32(), (h, a)), (sigma_next, "sigma_next", _f32(), (h, a)))
+    with _OnStream(stream) as st:
+        _check(load().cem_warm_start(ptrs[0], ptrs[1], h, a, mu_fill, sigma_fill, sigma_floor,
+                                     ptrs[2], ptrs[3], st))
 
 
 def mfma_ceiling(random_operands: bool = True, launches: int = 40):

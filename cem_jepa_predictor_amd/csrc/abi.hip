@@ -195,6 +195,23 @@ cem_status cem_sample(const float* mu, const float* sigma, int32_t n, int32_t h,
   });
 }
 
+cem_status cem_warm_start(const float* mu_prev, const float* sigma_prev, int32_t h, int32_t a,
+                          float mu_fill, float sigma_fill, float sigma_floor, float* mu_next,
+                          float* sigma_next, void* stream) {
+  return guarded([&]() -> cem_status {
+    if (!mu_prev || !sigma_prev || !mu_next || !sigma_next) return fail(CEM_E_ARG, "null argument");
+    if (!aligned(mu_prev, 4) || !aligned(sigma_prev, 4) || !aligned(mu_next, 4) || !aligned(sigma_next, 4))
+      return fail(CEM_E_ARG, "misaligned pointer");
+    if (h < 1 || a < 1 || (long long)h * a > 1024) return fail(CEM_E_SHAPE, "need h >= 1, a >= 1, h * a <= 1024");
+    if (!std::isfinite(mu_fill) || !std::isfinite(sigma_fill) || !(sigma_fill > 0.f) ||
+        !std::isfinite(sigma_floor) || sigma_floor < 0.f)
+      return fail(CEM_E_ARG, "need finite mu_fill, sigma_fill > 0 and finite sigma_floor >= 0");
+    return check_hip(cem::launch_warm_start(mu_prev, sigma_prev, h, a, mu_fill, sigma_fill, sigma_floor,
+                                            mu_next, sigma_next, static_cast<hipStream_t>(stream)),
+                     "warm-start kernel");
+  });
+}
+
 cem_status topk_select(const float* energy, int32_t n, int32_t k, int32_t* idx, void* stream) {
   return guarded([&]() -> cem_status {
     if (!energy || !idx) return fail(CEM_E_ARG, "null argument");

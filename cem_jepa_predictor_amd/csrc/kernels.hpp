@@ -79,6 +79,11 @@ hipError_t launch_energy(const T* zp, const float* g, int n, long long pe, float
 constexpr int kMaxSelect = 16384;
 hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int ha, int* idx,
                                float* mu, float* sigma, hipStream_t stream);
+// mu_next[t] = mu_prev[t + 1], sigma_next[t] = fmax(sigma_prev[t + 1], sigma_floor) for
+// t < h - 1; step h - 1 = (mu_fill, sigma_fill).  h * a <= 1024; outputs may alias inputs.
+hipError_t launch_warm_start(const float* mu_prev, const float* sigma_prev, int h, int a,
+                             float mu_fill, float sigma_fill, float sigma_floor, float* mu_next,
+                             float* sigma_next, hipStream_t stream);
 hipError_t select_init();
 
 // --- probe.hip -------------------------------------------------------------------

@@ -62,7 +62,40 @@ __global__ __launch_bounds__(1024) void select_refit_kernel(const float* __restr
   }
 }
 
+// Warm start of the next control step (page section 06, "B. Warm-started CEM"):
+// receding-horizon control executes only mu_R[0]; steps 1 .. h-1 of the plan seed
+// the next step's Gaussian, one step earlier, and the last step starts fresh.
+// One workgroup: every element is read before any is written, so the output may
+// alias the input.
+__global__ __launch_bounds__(1024) void warm_start_kernel(const float* mu_prev,
+                                                          const float* sigma_prev, int ha, int a,
+                                                          float mu_fill, float sigma_fill,
+                                                          float sigma_floor, float* mu_next,
+                                                          float* sigma_next) {
+  const int i = threadIdx.x;
+  float m = mu_fill, s = sigma_fill;
+  if (i + a < ha) {
+    m = mu_prev[i + a];
+    s = fmaxf(sigma_prev[i + a], sigma_floor);   // NaN width -> sigma_floor
+  }
+  __syncthreads();
+  if (i < ha) {
+    mu_next[i] = m;
+    sigma_next[i] = s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_warm_start(const float* mu_prev, const float* sigma_prev, int h, int a,
+                             float mu_fill, float sigma_fill, float sigma_floor, float* mu_next,
+                             float* sigma_next, hipStream_t stream) {
+  const int ha = h * a;
+  if (ha <= 0 || ha > 1024) return hipErrorInvalidValue;
+  warm_start_kernel<<<1, 1024, 0, stream>>>(mu_prev, sigma_prev, ha, a, mu_fill, sigma_fill,
+                                            sigma_floor, mu_next, sigma_next);
+  return hipGetLastError();
+}
 
 hipError_t select_init() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&select_refit_kernel),

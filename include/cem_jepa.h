@@ -159,6 +159,23 @@ cem_status elite_refit(const float* energy, const float* actions, int32_t n, int
                        int32_t h, int32_t a, int32_t* elite_idx, float* mu, float* sigma,
                        void* stream);
 
+/* Warm start of the next control step (page section 06, "B. Warm-started
+ * CEM"): receding-horizon control executes only the plan's first action; the
+ * rest of the plan seeds the next step's Gaussian, one step earlier, instead of
+ * a fresh one, so the next plan can converge in fewer rounds.
+ *   mu_prev, sigma_prev : device fp32 [h, a]  a plan's final mu, sigma
+ *   mu_next, sigma_next : device fp32 [h, a]  out (may alias the inputs)
+ * For t < h - 1: mu_next[t] = mu_prev[t + 1] and sigma_next[t] =
+ * fmax(sigma_prev[t + 1], sigma_floor) (a NaN width becomes sigma_floor); the
+ * last step starts fresh: mu_next[h - 1] = mu_fill, sigma_next[h - 1] =
+ * sigma_fill.  h = 1 is a plain reset.  sigma_floor = sigma_fill resets every
+ * width to at least the fresh one; 0 keeps the previous widths.
+ * h * a <= 1024; mu_fill, sigma_fill, sigma_floor finite, sigma_fill > 0,
+ * sigma_floor >= 0.  Pass the result as cem_plan's mu, sigma. */
+cem_status cem_warm_start(const float* mu_prev, const float* sigma_prev, int32_t h, int32_t a,
+                          float mu_fill, float sigma_fill, float sigma_floor, float* mu_next,
+                          float* sigma_next, void* stream);
+
 /* Sampler alone: actions[n, h, a] = clamp(mu + sigma * z, lo, hi) for round
  * `round` (see cem_plan); raw_words (nullable) receives each element's Philox
  * word, uint32 [n * h * a]. */

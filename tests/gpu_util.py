@@ -64,8 +64,9 @@ def release_models():
 
 def run_plan(name: str, *, use_graph: bool = True, rounds: int | None = None,
              n: int | None = None, k: int | None = None, seed: int | None = None,
-             plan_id: int = 0, horizon: int | None = None):
-    """Run cem_plan on the GPU and return outputs and the full trace as numpy."""
+             plan_id: int = 0, horizon: int | None = None, mu_init=None, sigma_init=None):
+    """Run cem_plan on the GPU and return outputs and the full trace as numpy.
+    mu_init / sigma_init [H, A] replace the fresh Gaussian when given."""
     import torch
 
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
@@ -76,6 +77,10 @@ def run_plan(name: str, *, use_graph: bool = True, rounds: int | None = None,
     model = gpu_model(name)
     mu = torch.full((H, A), pc.mu0, dtype=torch.float32, device="cuda")
     sigma = torch.full((H, A), pc.sigma0, dtype=torch.float32, device="cuda")
+    if mu_init is not None:
+        mu.copy_(torch.from_numpy(np.ascontiguousarray(mu_init, np.float32)))
+    if sigma_init is not None:
+        sigma.copy_(torch.from_numpy(np.ascontiguousarray(sigma_init, np.float32)))
     action = torch.empty(A, dtype=torch.float32, device="cuda")
     best = torch.empty(1, dtype=torch.int32, device="cuda")
     model.plan(to_dev(z_obs), to_dev(z_goal), to_dev(s0), mu, sigma, action, best, n_samples=N,

@@ -149,3 +149,14 @@ def test_binding_rejects_bad_tensors_before_the_library():
         _lib.topk_select(torch.zeros(4), 2, torch.zeros(2, dtype=torch.int64))
     with pytest.raises(TypeError, match="out: dtype torch.float32"):
         _lib.Model.trace(None, _lib.TRACE_ELITES, torch.zeros(4))
+
+
+def test_warm_start_validates_before_launch(lib):
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.cem_warm_start(None, fake, 2, 7, 0.0, 1.0, 0.0, fake, fake, None) == -1
+    assert lib.cem_warm_start(fake, fake, 0, 7, 0.0, 1.0, 0.0, fake, fake, None) == -2
+    assert lib.cem_warm_start(fake, fake, 200, 7, 0.0, 1.0, 0.0, fake, fake, None) == -2
+    assert lib.cem_warm_start(fake, fake, 2, 7, 0.0, 0.0, 0.0, fake, fake, None) == -1
+    assert lib.cem_warm_start(fake, fake, 2, 7, 0.0, 1.0, -0.5, fake, fake, None) == -1
+    assert lib.cem_warm_start(fake, fake, 2, 7, float("inf"), 1.0, 0.0, fake, fake, None) == -1
+    assert lib.cem_warm_start(fake, ctypes.c_void_p(0x1002), 2, 7, 0.0, 1.0, 0.0, fake, fake, None) == -1

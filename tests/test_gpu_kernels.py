@@ -177,3 +177,30 @@ def test_mfma_ceiling_probe_is_plausible(gpu_lib):
         # throughput and clock agree: 256 CUs x 4096 FLOP per clock at most
         assert tf <= 256 * 4096 * mhz * 1e6 / 1e12 * 1.05
     assert rt <= ct * 1.05
+
+
+@pytest.mark.parametrize("h,a,floor", [(1, 7, 0.0), (2, 7, 0.5), (8, 32, 0.0), (32, 32, 1.0)])
+def test_warm_start_bit_exact(gpu_lib, h, a, floor):
+    """cem_warm_start against the oracle's warm_start, out of place and in place
+    (h * a = 1024 is the largest accepted size)."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+    from oracle import cem
+
+    log(f"warm start h={h} a={a} floor={floor}")
+    rng = np.random.default_rng(h * 100 + a)
+    mu = rng.uniform(-1, 1, (h, a)).astype(np.float32)
+    sigma = rng.uniform(0, 1.5, (h, a)).astype(np.float32)
+    if h > 1:
+        sigma[1, 0] = np.nan
+        sigma[-1, -1] = 0.0
+    want_mu, want_sigma = cem.warm_start(mu, sigma, 0.125, 0.75, floor)
+    mt, st = to_dev(mu), to_dev(sigma)
+    mo = torch.full((h, a), 7.0, dtype=torch.float32, device="cuda")
+    so = torch.full((h, a), 7.0, dtype=torch.float32, device="cuda")
+    _lib.warm_start(mt, st, 0.125, 0.75, floor, mo, so)
+    _lib.warm_start(mt, st, 0.125, 0.75, floor, mt, st)   # in place
+    torch.cuda.synchronize()
+    for got_mu, got_sigma in ((mo, so), (mt, st)):
+        np.testing.assert_array_equal(to_np(got_mu), want_mu)
+        np.testing.assert_array_equal(to_np(got_sigma), want_sigma)

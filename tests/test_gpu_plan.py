@@ -76,17 +76,20 @@ def test_rollout_matches_oracle(gpu_lib, name, n):
             assert r >= 0.9999
 
 
-def _lockstep(name, out, oracle_rows):
+def _lockstep(name, out, oracle_rows, mu_init=None, sigma_init=None, plan_id=None):
     """Follow the GPU plan round by round with the oracle."""
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
     pc = wl.plan
     N, K, R, H = out["N"], out["K"], out["R"], out["H"]
     pred = oracle_predictor(name)
-    mu = np.full((H, 7), pc.mu0, np.float32)
-    sigma = np.full((H, 7), pc.sigma0, np.float32)
+    mu = np.full((H, 7), pc.mu0, np.float32) if mu_init is None else np.asarray(mu_init, np.float32)
+    sigma = np.full((H, 7), pc.sigma0, np.float32) if sigma_init is None else np.asarray(sigma_init, np.float32)
+    np.testing.assert_array_equal(out["mu"][0], mu)
+    np.testing.assert_array_equal(out["sigma"][0], sigma)
+    pid = pc.plan_id if plan_id is None else plan_id
     worst = 0.0
     for r in range(R):
-        x = o_sampler.sample_actions(mu, sigma, pc.seed, r, pc.plan_id, N, pc.clamp_lo, pc.clamp_hi)
+        x = o_sampler.sample_actions(mu, sigma, pc.seed, r, pid, N, pc.clamp_lo, pc.clamp_hi)
         # samples: identical up to a float32 ulp where float64 libms differ
         ulps = np.abs(out["x"][r].view(np.int32).astype(np.int64) - x.view(np.int32).astype(np.int64))
         assert ulps.max() <= 1, f"round {r}: samples differ by {ulps.max()} ulp"
@@ -222,3 +225,31 @@ def test_plan_shorter_horizon_than_max(gpu_lib):
     log("plan small with H=1 on a max-horizon-3 model")
     out = run_plan("small", horizon=1, rounds=2)
     _lockstep("small", out, lambda r, n: np.arange(4))
+
+
+@pytest.mark.parametrize("floor", [0.0, 1.0])
+def test_warm_started_closed_loop_lockstep(gpu_lib, floor):
+    """Receding-horizon control (page section 06 B): each control step's plan
+    starts from cem_warm_start of the previous plan (shifted one step, fresh last
+    step), run in place on the device; the warm start is bit-exact against the
+    oracle and every plan follows the oracle round by round."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+    from oracle import cem
+
+    wl = workload_data("tiny")[0]
+    pc = wl.plan
+    H, A = pc.horizon, wl.model.action_dim
+    mu = np.full((H, A), pc.mu0, np.float32)
+    sigma = np.full((H, A), pc.sigma0, np.float32)
+    log(f"warm-started closed loop, tiny, 3 control steps x 2 rounds, sigma floor {floor}")
+    for step in range(3):
+        out = run_plan("tiny", rounds=2, plan_id=step, mu_init=mu, sigma_init=sigma)
+        _lockstep("tiny", out, lambda r, n: np.arange(n), mu_init=mu, sigma_init=sigma, plan_id=step)
+        mt, st = to_dev(out["mu_out"]), to_dev(out["sigma_out"])
+        _lib.warm_start(mt, st, pc.mu0, pc.sigma0, floor, mt, st)
+        torch.cuda.synchronize()
+        mu, sigma = cem.warm_start(out["mu_out"], out["sigma_out"], pc.mu0, pc.sigma0, floor)
+        np.testing.assert_array_equal(to_np(mt), mu)
+        np.testing.assert_array_equal(to_np(st), sigma)
+        np.testing.assert_array_equal(mu[0], out["mu_out"][1])

@@ -105,3 +105,49 @@ def test_cem_follows_supplied_selection_energies():
                        select_energy_fn=rev)
     e0 = out["trace"]["energy"][0]
     assert list(out["trace"]["elites"][0]) == list(select.topk_elites(-e0, 8))
+
+
+def test_warm_start_closed_form():
+    """Next step's Gaussian: shift one step earlier, fresh last step, width floor."""
+    mu = np.array([[0.1, -0.2], [0.3, 0.4], [-0.5, 0.6]], np.float32)
+    sigma = np.array([[0.9, 0.8], [0.05, np.nan], [0.2, 0.0]], np.float32)
+    m, s = cem.warm_start(mu, sigma, 0.0, 1.0, 0.1)
+    np.testing.assert_array_equal(m, np.array([[0.3, 0.4], [-0.5, 0.6], [0.0, 0.0]], np.float32))
+    np.testing.assert_array_equal(s, np.array([[0.1, 0.1], [0.2, 0.1], [1.0, 1.0]], np.float32))
+    # floor 0 carries the widths; horizon 1 is a plain reset
+    _, s0 = cem.warm_start(mu, np.abs(np.nan_to_num(sigma)), 0.0, 1.0, 0.0)
+    np.testing.assert_array_equal(s0[:2], np.array([[0.05, 0.0], [0.2, 0.0]], np.float32))
+    m1, s1 = cem.warm_start(mu[:1], sigma[:1], 0.25, 0.5, 0.0)
+    np.testing.assert_array_equal(m1, [[0.25, 0.25]])
+    np.testing.assert_array_equal(s1, [[0.5, 0.5]])
+
+
+def _moving_quadratic(seed, steps, h, a):
+    """Target trajectory c[t] and, per control step s, the energy sum_t ||x_t - c[s + t]||^2."""
+    ph = np.random.default_rng(seed).uniform(0, 2 * np.pi, a)
+    c = 0.6 * np.sin(0.35 * np.arange(steps + h)[:, None] + ph)
+
+    def for_step(s):
+        tgt = c[s:s + h]
+        return lambda _r, x: ((x.astype(np.float64) - tgt) ** 2).sum(axis=(1, 2)).astype(np.float32)
+
+    return c, for_step
+
+
+def test_warm_started_three_rounds_track_like_cold_ten():
+    """Section 06 B on a closed-form receding-horizon task: after the first H
+    steps, a warm-started 3-round search executes actions about as close to the
+    target as a fresh 10-round search, and far closer than a fresh 3-round one.
+    A warm start that forgot the one-step shift lags the target by a step."""
+    h, a, n, k, steps = 4, 3, 64, 8, 12
+    err = {"cold10": [], "cold3": [], "warm3": []}
+    for seed in range(4):
+        c, for_step = _moving_quadratic(seed, steps, h, a)
+        for name, rounds, warm in (("cold10", 10, False), ("cold3", 3, False), ("warm3", 3, True)):
+            acts, _ = cem.receding_horizon(for_step, steps, n, k, rounds, h, a, 0.0, 1.0, 7 + seed,
+                                           -1.0, 1.0, warm)
+            err[name].append(np.abs(acts - c[:steps])[h:].mean())
+    e = {key: float(np.mean(v)) for key, v in err.items()}
+    assert e["warm3"] < 0.4 * e["cold3"], e
+    assert e["warm3"] < 2.5 * e["cold10"], e
+    assert e["warm3"] < 0.05, e
