@@ -18,6 +18,8 @@ all 10 rounds), inputs resident in HBM.  Prints ONE JSON line:
   cpu_baseline= the oracle (NumPy float64) on the host cores, on a bounded
                 sample of candidates, extrapolated to the metric's unit
 
+--batch B times fleet batching (section 06 C): B independent problems of N
+candidates each, planned by one cem_plan_batched call (value = B * N * R / time).
 --rounds R and --warm-start time the receding-horizon variant of section 06 B
 ("Warm-started CEM"): every timed plan starts from cem_warm_start of the
 previous plan's final Gaussian (one step earlier, fresh last step, widths kept
@@ -26,6 +28,7 @@ down to --sigma-floor) instead of the fresh Gaussian, with R rounds.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -229,6 +232,8 @@ def main() -> int:
     ap.add_argument("--workload", default="vjepa2ac")
     ap.add_argument("--samples", type=int, default=0, help="override N (sweep); K = N / 10")
     ap.add_argument("--rounds", type=int, default=0, help="override R (rounds per plan)")
+    ap.add_argument("--batch", type=int, default=1,
+                    help="plan this many independent problems together (cem_plan_batched)")
     ap.add_argument("--warm-start", action="store_true",
                     help="each plan starts from cem_warm_start of the previous one")
     ap.add_argument("--sigma-floor", type=float, default=0.0,
@@ -283,8 +288,6 @@ def main() -> int:
     else:
         wl = inputs.WORKLOADS[args.workload]
     if args.rounds:
-        import dataclasses
-
         wl = dataclasses.replace(wl, plan=dataclasses.replace(wl.plan, rounds=args.rounds))
     m, pc = wl.model, wl.plan
     N, K, R, H, A = pc.n_samples, pc.n_elites, pc.rounds, pc.horizon, m.action_dim
@@ -295,28 +298,37 @@ def main() -> int:
     flat = inputs.flatten_weights(m, w)
     del w
     z_obs, z_goal, s0 = inputs.make_embeddings(m, wl.embed_seed)
-    model = _lib.Model(m, flat, N)
+    NB = max(1, args.batch)
+    model = _lib.Model(m, flat, N * NB)
     del flat
     eprint(f"[bench] model ready in {time.perf_counter() - t0:.1f} s")
 
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()  # noqa: E731
     zo, zg, st = dev(z_obs), dev(z_goal), dev(s0)
-    mu0 = torch.full((H, A), pc.mu0, device="cuda")
-    sg0 = torch.full((H, A), pc.sigma0, device="cuda")
+    shp = (NB, H, A) if NB > 1 else (H, A)
+    mu0 = torch.full(shp, pc.mu0, device="cuda")
+    sg0 = torch.full(shp, pc.sigma0, device="cuda")
     mu, sg = mu0.clone(), sg0.clone()
-    action = torch.empty(A, device="cuda")
-    best = torch.empty(1, dtype=torch.int32, device="cuda")
+    action = torch.empty((NB, A) if NB > 1 else (A,), device="cuda")
+    best = torch.empty(NB, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    if NB > 1:   # every problem sees the same observation and goal (timing does not depend on them)
+        zo, zg, st = (t.unsqueeze(0).repeat(NB, *([1] * t.dim())).contiguous() for t in (zo, zg, st))
 
     def step(i: int, use_graph: bool = True):
         if args.warm_start:
+            if NB > 1:
+                raise SystemExit("--warm-start with --batch is not supported")
             _lib.warm_start(mu, sg, pc.mu0, pc.sigma0, args.sigma_floor, mu, sg, stream=stream)
         else:
             mu.copy_(mu0)
             sg.copy_(sg0)
-        model.plan(zo, zg, st, mu, sg, action, best, n_samples=N, n_elites=K, rounds=R, horizon=H,
-                   seed=pc.seed, plan_id=i, clamp_lo=pc.clamp_lo, clamp_hi=pc.clamp_hi,
-                   use_graph=use_graph, stream=stream)
+        kw = dict(n_samples=N, n_elites=K, rounds=R, horizon=H, seed=pc.seed, plan_id=i * NB,
+                  clamp_lo=pc.clamp_lo, clamp_hi=pc.clamp_hi, use_graph=use_graph, stream=stream)
+        if NB > 1:
+            model.plan_batched(zo, zg, st, mu, sg, action, best, **kw)
+        else:
+            model.plan(zo, zg, st, mu, sg, action, best, **kw)
 
     for i in range(args.warmup):
         step(i)
@@ -390,8 +402,9 @@ def main() -> int:
         eprint(f"[bench] timing the oracle on the host (~{args.cpu_seconds:.0f} s)")
         cpu = cpu_baseline(wl, args.cpu_seconds)
 
-    value = N * R / (ms * 1e-3)
-    plan_ms_roof = plan_roofline_ms(m, pc, MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS)
+    value = NB * N * R / (ms * 1e-3)
+    pc_all = dataclasses.replace(pc, n_samples=N * NB)   # a batch rolls out NB * N candidates a round
+    plan_ms_roof = plan_roofline_ms(m, pc_all, MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS)
     out = {
         "metric": "predictor candidate-evals/sec + ms per CEM plan step (800x10) on 1 MI355X",
         "value": round(value, 2), "unit": "candidate-evals/s", "n_gpus": 1, "steps": args.steps,
@@ -400,7 +413,7 @@ def main() -> int:
         "data": "synthetic: random-init weights N(0,0.02) (seed 0), N(0,1) embeddings (seed 1), "
                 "CEM seed 2",
         "config": {"workload": wl.name, "n_samples": N, "n_elites": K, "rounds": R, "horizon": H,
-                   "warm_start": bool(args.warm_start),
+                   "warm_start": bool(args.warm_start), "batch": NB,
                    "layers": m.layers, "d_model": m.d_model, "heads": m.heads, "d_mlp": m.d_mlp,
                    "patches": m.patches, "enc_dim": m.enc_dim, "graph_replay": True,
                    "eager_ms_per_step": round(eager_ms, 3) if eager_ms else None},

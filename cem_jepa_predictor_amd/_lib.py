@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYP
                 -4: "CEM_E_OOM", -5: "CEM_E_HIP", -6: "CEM_E_INTERNAL"}
 
 EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
-           "cem_plan", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
+           "cem_plan", "cem_plan_batched", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
            "cem_sample", "topk_select", "cem_warm_start", "cem_timer_enable", "cem_timer_read",
            "cem_mfma_ceiling"]
 
@@ -79,6 +79,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cem_model_create": [ctypes.POINTER(ModelDesc), P, SZ, I32, ctypes.POINTER(P)],
         "cem_model_destroy": [P],
         "cem_plan": [P, ctypes.POINTER(Params), P, P, P, P, P, P, P, P],
+        "cem_plan_batched": [P, ctypes.POINTER(Params), I32, P, P, P, P, P, P, P, P],
         "cem_plan_trace": [P, I32, P, SZ, P],
         "predictor_rollout": [P, P, I32, I32, P, P, P, P],
         "energy_l1": [P, I32, P, I32, I32, I32, P, P],
@@ -245,6 +246,27 @@ class Model:
                    1 if use_graph else 0)
         with _OnStream(stream) as st:
             _check(load().cem_plan(self.handle, ctypes.byref(p), *ptrs, st))
+        self._last = p
+
+    def plan_batched(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
+                     n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,
+                     clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True,
+                     stream=None):
+        """cem_plan_batched: z_obs/z_goal [b, P, E], s0 [b, S], mu/sigma [b, H, A],
+        action [b, A], best_idx [b]; problem i plans with plan id plan_id + i."""
+        c = self.cfg
+        if z_obs.dim() != 3:
+            raise ValueError(f"z_obs: expected [batch, P, E], got {tuple(z_obs.shape)}")
+        b = z_obs.shape[0]
+        pe, ha = (b, c.patches, c.enc_dim), (b, horizon, c.action_dim)
+        ptrs = _args((z_obs, "z_obs", _f32(), pe), (z_goal, "z_goal", _f32(), pe),
+                     (s0, "s0", _f32(), (b, c.state_dim)), (mu, "mu", _f32(), ha),
+                     (sigma, "sigma", _f32(), ha), (action, "action", _f32(), (b, c.action_dim)),
+                     (best_idx, "best_idx", _i32(), (b,), True))
+        p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
+                   1 if use_graph else 0)
+        with _OnStream(stream) as st:
+            _check(load().cem_plan_batched(self.handle, ctypes.byref(p), b, *ptrs, st))
         self._last = p
 
     def trace(self, kind: int, out, stream=None):

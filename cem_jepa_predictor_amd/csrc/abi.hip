@@ -58,6 +58,34 @@ cem_status check_hip(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace {
+cem_status plan_checked(cem_model* model, const cem_params* p, int32_t batch, const float* z_obs,
+                        const float* z_goal, const float* s0, float* mu, float* sigma, float* action,
+                        int32_t* best_idx, void* stream) {
+  if (!model || !p || !z_obs || !z_goal || !s0 || !mu || !sigma || !action)
+    return fail(CEM_E_ARG, "null argument");
+  if (!aligned(z_obs, 4) || !aligned(z_goal, 4) || !aligned(s0, 4) || !aligned(mu, 4) ||
+      !aligned(sigma, 4) || !aligned(action, 4) || (best_idx && !aligned(best_idx, 4)))
+    return fail(CEM_E_ARG, "misaligned pointer (4-byte alignment required)");
+  const cem_model_desc& d = model->desc;
+  if (batch < 1 || batch > 4096) return fail(CEM_E_SHAPE, "batch must be in [1, 4096]");
+  if (p->n_samples < 1 || (long long)p->n_samples * batch > d.max_samples)
+    return fail(CEM_E_SHAPE, "n_samples must be >= 1 with batch * n_samples <= max_samples");
+  if (p->n_elites < 1 || p->n_elites > p->n_samples)
+    return fail(CEM_E_SHAPE, "n_elites must be in [1, n_samples]");
+  if (p->rounds < 1 || p->rounds > 4096) return fail(CEM_E_SHAPE, "rounds must be in [1, 4096]");
+  if (p->horizon < 1 || p->horizon > d.max_horizon)
+    return fail(CEM_E_SHAPE, "horizon must be in [1, max_horizon]");
+  if (!std::isfinite(p->clamp_lo) || !std::isfinite(p->clamp_hi) || p->clamp_lo > p->clamp_hi)
+    return fail(CEM_E_ARG, "clamp bounds must be finite with lo <= hi");
+  if (p->use_graph != 0 && p->use_graph != 1) return fail(CEM_E_ARG, "use_graph must be 0 or 1");
+  if ((uint64_t)p->plan_id + (uint64_t)(batch - 1) > 0xffffffffull)
+    return fail(CEM_E_ARG, "plan_id + batch - 1 must fit in 32 bits");
+  return finish(cem::plan(model, *p, batch, z_obs, z_goal, s0, mu, sigma, action, best_idx,
+                          static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
 extern "C" {
 
 const char* cem_last_error(void) { return g_last_error.c_str(); }
@@ -97,28 +125,20 @@ cem_status cem_model_destroy(cem_model* model) {
   });
 }
 
+
 cem_status cem_plan(cem_model* model, const cem_params* p, const float* z_obs, const float* z_goal,
                     const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
                     void* stream) {
   return guarded([&]() -> cem_status {
-    if (!model || !p || !z_obs || !z_goal || !s0 || !mu || !sigma || !action)
-      return fail(CEM_E_ARG, "null argument");
-    if (!aligned(z_obs, 4) || !aligned(z_goal, 4) || !aligned(s0, 4) || !aligned(mu, 4) ||
-        !aligned(sigma, 4) || !aligned(action, 4) || (best_idx && !aligned(best_idx, 4)))
-      return fail(CEM_E_ARG, "misaligned pointer (4-byte alignment required)");
-    const cem_model_desc& d = model->desc;
-    if (p->n_samples < 1 || p->n_samples > d.max_samples)
-      return fail(CEM_E_SHAPE, "n_samples must be in [1, max_samples]");
-    if (p->n_elites < 1 || p->n_elites > p->n_samples)
-      return fail(CEM_E_SHAPE, "n_elites must be in [1, n_samples]");
-    if (p->rounds < 1 || p->rounds > 4096) return fail(CEM_E_SHAPE, "rounds must be in [1, 4096]");
-    if (p->horizon < 1 || p->horizon > d.max_horizon)
-      return fail(CEM_E_SHAPE, "horizon must be in [1, max_horizon]");
-    if (!std::isfinite(p->clamp_lo) || !std::isfinite(p->clamp_hi) || p->clamp_lo > p->clamp_hi)
-      return fail(CEM_E_ARG, "clamp bounds must be finite with lo <= hi");
-    if (p->use_graph != 0 && p->use_graph != 1) return fail(CEM_E_ARG, "use_graph must be 0 or 1");
-    return finish(cem::plan(model, *p, z_obs, z_goal, s0, mu, sigma, action, best_idx,
-                            static_cast<hipStream_t>(stream)));
+    return plan_checked(model, p, 1, z_obs, z_goal, s0, mu, sigma, action, best_idx, stream);
+  });
+}
+
+cem_status cem_plan_batched(cem_model* model, const cem_params* p, int32_t batch, const float* z_obs,
+                            const float* z_goal, const float* s0, float* mu, float* sigma,
+                            float* action, int32_t* best_idx, void* stream) {
+  return guarded([&]() -> cem_status {
+    return plan_checked(model, p, batch, z_obs, z_goal, s0, mu, sigma, action, best_idx, stream);
   });
 }
 
@@ -155,8 +175,8 @@ cem_status energy_l1(const void* z_pred, int32_t dtype, const float* z_goal, int
     const long long pe = (long long)p * e;
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t r =
-        dtype == CEM_BF16 ? cem::launch_energy<cem::bf16>(static_cast<const cem::bf16*>(z_pred), z_goal, n, pe, energy, st)
-                          : cem::launch_energy<float>(static_cast<const float*>(z_pred), z_goal, n, pe, energy, st);
+        dtype == CEM_BF16 ? cem::launch_energy<cem::bf16>(static_cast<const cem::bf16*>(z_pred), z_goal, n, pe, energy, n, st)
+                          : cem::launch_energy<float>(static_cast<const float*>(z_pred), z_goal, n, pe, energy, n, st);
     return check_hip(r, "energy kernel");
   });
 }

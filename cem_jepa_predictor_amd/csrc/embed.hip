@@ -29,10 +29,11 @@ template <typename T>
 __global__ __launch_bounds__(256) void embed_action_state_kernel(
     const float* __restrict__ X, int H, int t, int A, int S, const float* __restrict__ s0,
     const float* __restrict__ wa, const float* __restrict__ ba, const float* __restrict__ ws,
-    const float* __restrict__ bs, T* __restrict__ x, int B, int d) {
+    const float* __restrict__ bs, T* __restrict__ x, int B, int d, int n_per) {
   __shared__ float act[32];
   __shared__ float st[32];
   const int n = blockIdx.x;
+  s0 += (long long)(n / n_per) * S;   // this candidate's problem
   const float* xn = X + (long long)n * H * A;
   if (threadIdx.x < A) act[threadIdx.x] = xn[t * A + threadIdx.x];
   if (threadIdx.x < S) {
@@ -56,9 +57,11 @@ __global__ __launch_bounds__(256) void embed_action_state_kernel(
 // grid: (ceil(P*d/8 / 256), N); 16-byte copies when rows are 16-byte multiples.
 template <typename T>
 __global__ __launch_bounds__(256) void broadcast_frame_kernel(const T* __restrict__ f0, int P,
-                                                              int d, T* __restrict__ x, int B) {
+                                                              int d, T* __restrict__ x, int B,
+                                                              int n_per) {
   constexpr int V = 16 / sizeof(T);
   const int n = blockIdx.y;
+  f0 += (long long)(n / n_per) * P * d;   // this candidate's problem
   const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * V;
   if (i >= (long long)P * d) return;
   const int p = (int)(i / d), j = (int)(i % d);
@@ -79,20 +82,23 @@ template <typename T>
 hipError_t launch_embed_action_state(const float* X, int N, int H, int t, int A, int S,
                                      const float* s0, const float* wa, const float* ba,
                                      const float* ws, const float* bs, T* x, int B, int d,
-                                     hipStream_t stream) {
+                                     int n_per, hipStream_t stream) {
   if (N <= 0) return hipSuccess;
-  embed_action_state_kernel<T><<<N, 256, 0, stream>>>(X, H, t, A, S, s0, wa, ba, ws, bs, x, B, d);
+  if (n_per <= 0) return hipErrorInvalidValue;
+  embed_action_state_kernel<T><<<N, 256, 0, stream>>>(X, H, t, A, S, s0, wa, ba, ws, bs, x, B, d,
+                                                      n_per);
   return hipGetLastError();
 }
 
 template <typename T>
-hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B,
+hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B, int n_per,
                                   hipStream_t stream) {
   if (N <= 0) return hipSuccess;
+  if (n_per <= 0) return hipErrorInvalidValue;
   constexpr int V = 16 / sizeof(T);
   const long long vec = (long long)P * d / V;   // d % 64 == 0, so rows are whole vectors
   dim3 grid((unsigned)((vec + 255) / 256), (unsigned)N);
-  broadcast_frame_kernel<T><<<grid, 256, 0, stream>>>(f0, P, d, x, B);
+  broadcast_frame_kernel<T><<<grid, 256, 0, stream>>>(f0, P, d, x, B, n_per);
   return hipGetLastError();
 }
 
@@ -101,8 +107,9 @@ hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B,
   template hipError_t launch_embed_action_state<T>(const float*, int, int, int, int, int,       \
                                                    const float*, const float*, const float*,    \
                                                    const float*, const float*, T*, int, int,    \
-                                                   hipStream_t);                                \
-  template hipError_t launch_broadcast_frame<T>(const T*, int, int, T*, int, int, hipStream_t);
+                                                   int, hipStream_t);                           \
+  template hipError_t launch_broadcast_frame<T>(const T*, int, int, T*, int, int, int,          \
+                                                hipStream_t);
 INST(float)
 INST(bf16)
 #undef INST

@@ -45,9 +45,10 @@ template <> struct Vec8<float> {
 template <typename T, bool VEC>
 __global__ __launch_bounds__(256) void energy_kernel(const T* __restrict__ zp,
                                                      const float* __restrict__ g, long long pe,
-                                                     float* __restrict__ E) {
+                                                     float* __restrict__ E, int n_per) {
   __shared__ float part[4];
   const T* z = zp + (long long)blockIdx.x * pe;
+  g += (long long)(blockIdx.x / n_per) * pe;   // this candidate's problem
   float acc = 0.f;
   if (VEC) {
     for (long long j = (long long)threadIdx.x * 8; j < pe; j += 256 * 8)
@@ -68,20 +69,21 @@ __global__ __launch_bounds__(256) void energy_kernel(const T* __restrict__ zp,
 }  // namespace
 
 template <typename T>
-hipError_t launch_energy(const T* zp, const float* g, int n, long long pe, float* E,
+hipError_t launch_energy(const T* zp, const float* g, int n, long long pe, float* E, int n_per,
                          hipStream_t stream) {
   if (n <= 0) return hipSuccess;
+  if (n_per <= 0) return hipErrorInvalidValue;
   const bool vec = (pe % 8 == 0) && ((uintptr_t)zp % 16 == 0) && ((uintptr_t)g % 16 == 0);
   if (vec)
-    energy_kernel<T, true><<<n, 256, 0, stream>>>(zp, g, pe, E);
+    energy_kernel<T, true><<<n, 256, 0, stream>>>(zp, g, pe, E, n_per);
   else
-    energy_kernel<T, false><<<n, 256, 0, stream>>>(zp, g, pe, E);
+    energy_kernel<T, false><<<n, 256, 0, stream>>>(zp, g, pe, E, n_per);
   return hipGetLastError();
 }
 
-template hipError_t launch_energy<float>(const float*, const float*, int, long long, float*,
+template hipError_t launch_energy<float>(const float*, const float*, int, long long, float*, int,
                                          hipStream_t);
-template hipError_t launch_energy<bf16>(const bf16*, const float*, int, long long, float*,
+template hipError_t launch_energy<bf16>(const bf16*, const float*, int, long long, float*, int,
                                         hipStream_t);
 
 }  // namespace cem

@@ -13,9 +13,11 @@ constexpr int kMaxBlocks = 8;   // frame blocks a query can attend (max horizon)
 // x[e] = clamp(mu[e % ha] + sigma[e % ha] * z[e], lo, hi), e < n * ha.
 // dev_params (nullable): uint32 {seed_lo, seed_hi, plan_id} overriding the
 // scalar arguments, so a captured graph can be re-keyed without re-capture.
+// batch > 1: problem b samples with mu + b ha, sigma + b ha and plan id + b into
+// x + b n ha (raw likewise), exactly as a batch-1 call with those arguments.
 hipError_t launch_sample(const float* mu, const float* sigma, int n, int ha, uint64_t seed,
                          uint32_t round, uint32_t plan_id, const uint32_t* dev_params, float lo,
-                         float hi, float* x, uint32_t* raw, hipStream_t stream);
+                         float hi, float* x, uint32_t* raw, hipStream_t stream, int batch = 1);
 hipError_t launch_set_params(uint32_t* dev_params, uint64_t seed, uint32_t plan_id,
                              hipStream_t stream);
 
@@ -23,14 +25,15 @@ hipError_t launch_set_params(uint32_t* dev_params, uint64_t seed, uint32_t plan_
 template <typename T>
 hipError_t launch_convert(const float* in, T* out, long long count, hipStream_t stream);
 // Action and state token rows (rows n*B + 0 and n*B + 1 of x) for step t.
+// Candidate n belongs to problem n / n_per, whose state is s0 + (n / n_per) S.
 template <typename T>
 hipError_t launch_embed_action_state(const float* X, int N, int H, int t, int A, int S,
                                      const float* s0, const float* wa, const float* ba,
                                      const float* ws, const float* bs, T* x, int B, int d,
-                                     hipStream_t stream);
-// Frame rows n*B + 2 + p of x = f0[p] for every candidate n.
+                                     int n_per, hipStream_t stream);
+// Frame rows n*B + 2 + p of x = f0[(n / n_per) P + p] for every candidate n.
 template <typename T>
-hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B,
+hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B, int n_per,
                                   hipStream_t stream);
 
 // --- layernorm.hip -----------------------------------------------------------
@@ -69,16 +72,18 @@ bool attention_bf16_supports(int dh, int B);
 bool attention_f32_supports(int dh);
 
 // --- energy.hip ----------------------------------------------------------------
+// E[i] = mean |zp[i] - g[(i / n_per) pe ...]| over pe elements.
 template <typename T>
-hipError_t launch_energy(const T* zp, const float* g, int n, long long pe, float* E,
+hipError_t launch_energy(const T* zp, const float* g, int n, long long pe, float* E, int n_per,
                          hipStream_t stream);
 
 // --- select_refit.hip ---------------------------------------------------------------
 // idx[k] = k smallest (E, index) pairs; if mu != nullptr also the elites'
-// mean / population std over ha columns of X [n, ha].
+// mean / population std over ha columns of X [n, ha].  batch > 1: problem b
+// works on E + b n, X + b n ha into idx + b k, mu + b ha, sigma + b ha.
 constexpr int kMaxSelect = 16384;
 hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int ha, int* idx,
-                               float* mu, float* sigma, hipStream_t stream);
+                               float* mu, float* sigma, hipStream_t stream, int batch = 1);
 // mu_next[t] = mu_prev[t + 1], sigma_next[t] = fmax(sigma_prev[t + 1], sigma_floor) for
 // t < h - 1; step h - 1 = (mu_fill, sigma_fill).  h * a <= 1024; outputs may alias inputs.
 hipError_t launch_warm_start(const float* mu_prev, const float* sigma_prev, int h, int a,

@@ -294,20 +294,24 @@ void* kv_slot(cem_model* m, int l, int tau, int horizon) {
   return static_cast<uint8_t*>(m->kv) + slot * (size_t)m->rows_max * 2 * m->desc.d_model * m->esz;
 }
 
-// f0 = z_obs W_in + b_in, shared by every candidate's first frame block.
+// f0 = z_obs W_in + b_in for each of `problems` observations [problems, P, E],
+// shared by every candidate's first frame block of that problem.
 template <typename T>
-hipError_t enqueue_frame0(cem_model* m, const float* z_obs, hipStream_t st) {
+hipError_t enqueue_frame0(cem_model* m, const float* z_obs, int problems, void* zobs_t, void* f0,
+                          hipStream_t st) {
   const int P = m->desc.patches, E = m->desc.enc_dim, D = m->desc.d_model;
   // stage z_obs (caller memory, 4-byte aligned) into the aligned model-dtype buffer
-  hipError_t r = launch_convert<T>(z_obs, static_cast<T*>(m->zobs_t), (long long)P * E, st);
+  hipError_t r = launch_convert<T>(z_obs, static_cast<T*>(zobs_t), (long long)problems * P * E, st);
   if (r != hipSuccess) return r;
-  return gemm(m, m->zobs_t, E, m->w_in_t, E, P, D, E, epi(m->b_in, m->f0, D, D), st);
+  return gemm(m, zobs_t, E, m->w_in_t, E, problems * P, D, E, epi(m->b_in, f0, D, D), st);
 }
 
 // Autoregressive block-causal rollout of n candidates; leaves z_H in m->zhat.
+// Candidate i belongs to problem i / n_per: state s0 + (i / n_per) S, frame-0
+// tokens f0 + (i / n_per) P d.
 template <typename T>
 hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const float* s0,
-                           hipStream_t st) {
+                           const void* f0, int n_per, hipStream_t st) {
   const cem_model_desc& d = m->desc;
   const int B = m->B, P = d.patches, D = d.d_model, F = d.d_mlp, E = d.enc_dim;
   const int rows = n * B;
@@ -315,9 +319,10 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
 #define RUN(x) do { r = (x); if (r != hipSuccess) return r; } while (0)
   for (int t = 0; t < H; ++t) {
     RUN(launch_embed_action_state<T>(X, n, H, t, d.action_dim, d.state_dim, s0, m->w_a, m->b_a,
-                                     m->w_s, m->b_s, static_cast<T*>(m->x), B, D, st));
+                                     m->w_s, m->b_s, static_cast<T*>(m->x), B, D, n_per, st));
     if (t == 0) {
-      RUN(launch_broadcast_frame<T>(static_cast<const T*>(m->f0), P, D, static_cast<T*>(m->x), n, B, st));
+      RUN(launch_broadcast_frame<T>(static_cast<const T*>(f0), P, D, static_cast<T*>(m->x), n, B,
+                                    n_per, st));
     } else {
       // frame rows of block t = previous prediction projected in (row r -> n B + 2 + p)
       RUN(gemm(m, m->zhat, E, m->w_in_t, E, n * P, D, E,
@@ -352,41 +357,46 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
 }
 
 template <typename T>
-hipError_t enqueue_plan_body(cem_model* m, const cem_params& p, hipStream_t st) {
+hipError_t enqueue_plan_body(cem_model* m, const cem_params& p, int batch, hipStream_t st) {
   PlanState& ps = m->plan;
   const int N = p.n_samples, K = p.n_elites, H = p.horizon, ha = H * m->desc.action_dim;
+  const int NB = batch * N;
   const long long pe = (long long)m->desc.patches * m->desc.enc_dim;
-  hipError_t r = enqueue_frame0<T>(m, ps.zobs, st);
+  hipError_t r = enqueue_frame0<T>(m, ps.zobs, batch, ps.zobs_t, ps.f0, st);
   if (r != hipSuccess) return r;
   for (int rd = 0; rd < p.rounds; ++rd) {
-    float* x = ps.x_hist + (size_t)rd * N * ha;
-    r = launch_sample(ps.mu_hist + (size_t)rd * ha, ps.sigma_hist + (size_t)rd * ha, N, ha, p.seed,
-                      (uint32_t)rd, p.plan_id, ps.params, p.clamp_lo, p.clamp_hi, x, nullptr, st);
+    float* x = ps.x_hist + (size_t)rd * NB * ha;
+    float* mu_rd = ps.mu_hist + (size_t)rd * batch * ha;
+    float* sg_rd = ps.sigma_hist + (size_t)rd * batch * ha;
+    r = launch_sample(mu_rd, sg_rd, N, ha, p.seed, (uint32_t)rd, p.plan_id, ps.params, p.clamp_lo,
+                      p.clamp_hi, x, nullptr, st, batch);
     if (r != hipSuccess) return r;
-    r = enqueue_rollout<T>(m, x, N, H, ps.s0, st);
+    r = enqueue_rollout<T>(m, x, NB, H, ps.s0, ps.f0, N, st);
     if (r != hipSuccess) return r;
-    r = launch_energy<T>(static_cast<const T*>(m->zhat), ps.zgoal, N, pe, ps.e_hist + (size_t)rd * N, st);
+    r = launch_energy<T>(static_cast<const T*>(m->zhat), ps.zgoal, NB, pe, ps.e_hist + (size_t)rd * NB, N, st);
     if (r != hipSuccess) return r;
-    r = launch_select_refit(ps.e_hist + (size_t)rd * N, x, N, K, ha, ps.elites + (size_t)rd * K,
-                            ps.mu_hist + (size_t)(rd + 1) * ha, ps.sigma_hist + (size_t)(rd + 1) * ha, st);
+    r = launch_select_refit(ps.e_hist + (size_t)rd * NB, x, N, K, ha, ps.elites + (size_t)rd * batch * K,
+                            mu_rd + (size_t)batch * ha, sg_rd + (size_t)batch * ha, st, batch);
     if (r != hipSuccess) return r;
   }
   return hipSuccess;
 }
 
-Status ensure_plan_state(cem_model* m, const cem_params& p) {
+Status ensure_plan_state(cem_model* m, const cem_params& p, int batch) {
   PlanState& ps = m->plan;
   const int ha = p.horizon * m->desc.action_dim;
-  if (ps.mem && p.n_samples <= ps.n && p.n_elites <= ps.k && p.rounds <= ps.r && ha <= ps.ha)
+  if (ps.mem && p.n_samples <= ps.n && p.n_elites <= ps.k && p.rounds <= ps.r && ha <= ps.ha &&
+      batch <= ps.batch)
     return Status::Ok();
   const int n = std::max(p.n_samples, ps.n), k = std::max(p.n_elites, ps.k);
-  const int r = std::max(p.rounds, ps.r), hh = std::max(ha, ps.ha);
-  const size_t PE = (size_t)m->desc.patches * m->desc.enc_dim;
+  const int r = std::max(p.rounds, ps.r), hh = std::max(ha, ps.ha), nb = std::max(batch, ps.batch);
+  const size_t P = m->desc.patches, PE = P * m->desc.enc_dim, PD = P * m->desc.d_model;
   Layout l;
-  const size_t o_x = l.take((size_t)r * n * hh * 4), o_e = l.take((size_t)r * n * 4);
-  const size_t o_mu = l.take((size_t)(r + 1) * hh * 4), o_sg = l.take((size_t)(r + 1) * hh * 4);
-  const size_t o_el = l.take((size_t)r * k * 4);
-  const size_t o_zo = l.take(PE * 4), o_zg = l.take(PE * 4), o_s0 = l.take(64 * 4), o_pp = l.take(16);
+  const size_t o_x = l.take((size_t)r * nb * n * hh * 4), o_e = l.take((size_t)r * nb * n * 4);
+  const size_t o_mu = l.take((size_t)(r + 1) * nb * hh * 4), o_sg = l.take((size_t)(r + 1) * nb * hh * 4);
+  const size_t o_el = l.take((size_t)r * nb * k * 4);
+  const size_t o_zo = l.take(nb * PE * 4), o_zg = l.take(nb * PE * 4), o_s0 = l.take((size_t)nb * 64 * 4);
+  const size_t o_zt = l.take(nb * PE * m->esz), o_f0 = l.take(nb * PD * m->esz), o_pp = l.take(16);
   // existing graphs reference the old buffers
   CEM_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
@@ -394,26 +404,27 @@ Status ensure_plan_state(cem_model* m, const cem_params& p) {
   if (ps.mem) { (void)hipFree(ps.mem); ps.mem = nullptr; }
   CEM_TRY(hipMalloc(&ps.mem, l.off), "hipMalloc(plan state)");
   uint8_t* b = static_cast<uint8_t*>(ps.mem);
-  ps.n = n; ps.k = k; ps.r = r; ps.ha = hh;
+  ps.n = n; ps.k = k; ps.r = r; ps.ha = hh; ps.batch = nb;
   ps.x_hist = (float*)(b + o_x); ps.e_hist = (float*)(b + o_e);
   ps.mu_hist = (float*)(b + o_mu); ps.sigma_hist = (float*)(b + o_sg);
   ps.elites = (int*)(b + o_el);
   ps.zobs = (float*)(b + o_zo); ps.zgoal = (float*)(b + o_zg); ps.s0 = (float*)(b + o_s0);
+  ps.zobs_t = b + o_zt; ps.f0 = b + o_f0;
   ps.params = (uint32_t*)(b + o_pp);
   return Status::Ok();
 }
 
 template <typename T>
-Status run_plan(cem_model* m, const cem_params& p, hipStream_t st) {
-  if (!p.use_graph || m->timers) return hip_status(enqueue_plan_body<T>(m, p, st), "plan kernels");
+Status run_plan(cem_model* m, const cem_params& p, int batch, hipStream_t st) {
+  if (!p.use_graph || m->timers) return hip_status(enqueue_plan_body<T>(m, p, batch, st), "plan kernels");
   uint32_t lo_bits, hi_bits;
   std::memcpy(&lo_bits, &p.clamp_lo, 4);
   std::memcpy(&hi_bits, &p.clamp_hi, 4);
-  const GraphKey key{p.n_samples, p.n_elites, p.rounds, p.horizon, lo_bits, hi_bits};
+  const GraphKey key{p.n_samples, p.n_elites, p.rounds, p.horizon, lo_bits, hi_bits, batch};
   auto it = m->graphs.find(key);
   if (it == m->graphs.end()) {
     CEM_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-    const hipError_t body = enqueue_plan_body<T>(m, p, m->cap_stream);
+    const hipError_t body = enqueue_plan_body<T>(m, p, batch, m->cap_stream);
     hipGraph_t g = nullptr;
     const hipError_t end = hipStreamEndCapture(m->cap_stream, &g);
     if (body != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_status(body, "plan capture"); }
@@ -433,42 +444,47 @@ Status run_plan(cem_model* m, const cem_params& p, hipStream_t st) {
 Status rollout(cem_model* m, const float* actions, int n, int horizon, const float* z_obs,
                const float* s0, void* z_pred, hipStream_t st) {
   DeviceGuard guard(m->device);
-  hipError_t r = m->bf16 ? enqueue_frame0<bf16>(m, z_obs, st) : enqueue_frame0<float>(m, z_obs, st);
+  hipError_t r = m->bf16 ? enqueue_frame0<bf16>(m, z_obs, 1, m->zobs_t, m->f0, st)
+                         : enqueue_frame0<float>(m, z_obs, 1, m->zobs_t, m->f0, st);
   if (r != hipSuccess) return hip_status(r, "frame projection");
-  r = m->bf16 ? enqueue_rollout<bf16>(m, actions, n, horizon, s0, st)
-              : enqueue_rollout<float>(m, actions, n, horizon, s0, st);
+  r = m->bf16 ? enqueue_rollout<bf16>(m, actions, n, horizon, s0, m->f0, n, st)
+              : enqueue_rollout<float>(m, actions, n, horizon, s0, m->f0, n, st);
   if (r != hipSuccess) return hip_status(r, "rollout kernels");
   const size_t bytes = (size_t)n * m->desc.patches * m->desc.enc_dim * m->esz;
   CEM_TRY(hipMemcpyAsync(z_pred, m->zhat, bytes, hipMemcpyDeviceToDevice, st), "hipMemcpyAsync(z_pred)");
   return Status::Ok();
 }
 
-Status plan(cem_model* m, const cem_params& p, const float* z_obs, const float* z_goal,
+Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, const float* z_goal,
             const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
             hipStream_t st) {
   DeviceGuard guard(m->device);
-  Status s = ensure_plan_state(m, p);
+  Status s = ensure_plan_state(m, p, batch);
   if (!s.ok()) return s;
   PlanState& ps = m->plan;
-  const size_t PE = (size_t)m->desc.patches * m->desc.enc_dim;
-  const int A = m->desc.action_dim, ha = p.horizon * A;
-  CEM_TRY(hipMemcpyAsync(ps.zobs, z_obs, PE * 4, hipMemcpyDeviceToDevice, st), "copy z_obs");
-  CEM_TRY(hipMemcpyAsync(ps.zgoal, z_goal, PE * 4, hipMemcpyDeviceToDevice, st), "copy z_goal");
-  CEM_TRY(hipMemcpyAsync(ps.s0, s0, (size_t)m->desc.state_dim * 4, hipMemcpyDeviceToDevice, st), "copy s0");
-  CEM_TRY(hipMemcpyAsync(ps.mu_hist, mu, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy mu");
-  CEM_TRY(hipMemcpyAsync(ps.sigma_hist, sigma, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma");
+  const size_t PE = (size_t)m->desc.patches * m->desc.enc_dim, S = m->desc.state_dim;
+  const int A = m->desc.action_dim, ha = p.horizon * A, K = p.n_elites;
+  const size_t nb = (size_t)batch;
+  CEM_TRY(hipMemcpyAsync(ps.zobs, z_obs, nb * PE * 4, hipMemcpyDeviceToDevice, st), "copy z_obs");
+  CEM_TRY(hipMemcpyAsync(ps.zgoal, z_goal, nb * PE * 4, hipMemcpyDeviceToDevice, st), "copy z_goal");
+  CEM_TRY(hipMemcpyAsync(ps.s0, s0, nb * S * 4, hipMemcpyDeviceToDevice, st), "copy s0");
+  CEM_TRY(hipMemcpyAsync(ps.mu_hist, mu, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy mu");
+  CEM_TRY(hipMemcpyAsync(ps.sigma_hist, sigma, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma");
   CEM_TRY(launch_set_params(ps.params, p.seed, p.plan_id, st), "set params");
-  s = m->bf16 ? run_plan<bf16>(m, p, st) : run_plan<float>(m, p, st);
+  s = m->bf16 ? run_plan<bf16>(m, p, batch, st) : run_plan<float>(m, p, batch, st);
   if (!s.ok()) return s;
-  const float* mu_r = ps.mu_hist + (size_t)p.rounds * ha;
-  const float* sg_r = ps.sigma_hist + (size_t)p.rounds * ha;
-  CEM_TRY(hipMemcpyAsync(mu, mu_r, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy mu out");
-  CEM_TRY(hipMemcpyAsync(sigma, sg_r, (size_t)ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma out");
-  CEM_TRY(hipMemcpyAsync(action, mu_r, (size_t)A * 4, hipMemcpyDeviceToDevice, st), "copy action");
+  const float* mu_r = ps.mu_hist + (size_t)p.rounds * nb * ha;
+  const float* sg_r = ps.sigma_hist + (size_t)p.rounds * nb * ha;
+  CEM_TRY(hipMemcpyAsync(mu, mu_r, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy mu out");
+  CEM_TRY(hipMemcpyAsync(sigma, sg_r, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma out");
+  // problem b's action = mu_R[b][0, :], best candidate = its last round's first elite
+  CEM_TRY(hipMemcpy2DAsync(action, (size_t)A * 4, mu_r, (size_t)ha * 4, (size_t)A * 4, nb,
+                           hipMemcpyDeviceToDevice, st), "copy action");
   if (best_idx)
-    CEM_TRY(hipMemcpyAsync(best_idx, ps.elites + (size_t)(p.rounds - 1) * p.n_elites, 4,
-                           hipMemcpyDeviceToDevice, st), "copy best_idx");
+    CEM_TRY(hipMemcpy2DAsync(best_idx, 4, ps.elites + (size_t)(p.rounds - 1) * nb * K, (size_t)K * 4, 4, nb,
+                             hipMemcpyDeviceToDevice, st), "copy best_idx");
   ps.last_n = p.n_samples; ps.last_k = p.n_elites; ps.last_r = p.rounds; ps.last_h = p.horizon;
+  ps.last_batch = batch;
   return Status::Ok();
 }
 
@@ -478,15 +494,16 @@ Status plan_trace(cem_model* m, int kind, void* dst, size_t bytes, hipStream_t s
   Status bad;
   bad.code = CEM_E_ARG;
   if (!ps.mem || ps.last_r == 0) { bad.msg = "no plan has run on this model"; return bad; }
-  const size_t N = ps.last_n, K = ps.last_k, R = ps.last_r, ha = (size_t)ps.last_h * m->desc.action_dim;
+  const size_t NB = (size_t)ps.last_batch, N = ps.last_n * NB, K = ps.last_k * NB, R = ps.last_r;
+  const size_t ha = (size_t)ps.last_h * m->desc.action_dim;
   const void* src = nullptr;
   size_t want = 0;
   switch (kind) {
     case CEM_TRACE_ACTIONS: src = ps.x_hist; want = R * N * ha * 4; break;
     case CEM_TRACE_ENERGY: src = ps.e_hist; want = R * N * 4; break;
     case CEM_TRACE_ELITES: src = ps.elites; want = R * K * 4; break;
-    case CEM_TRACE_MU: src = ps.mu_hist; want = (R + 1) * ha * 4; break;
-    case CEM_TRACE_SIGMA: src = ps.sigma_hist; want = (R + 1) * ha * 4; break;
+    case CEM_TRACE_MU: src = ps.mu_hist; want = (R + 1) * NB * ha * 4; break;
+    case CEM_TRACE_SIGMA: src = ps.sigma_hist; want = (R + 1) * NB * ha * 4; break;
     default: bad.msg = "unknown trace kind"; return bad;
   }
   if (bytes != want) {

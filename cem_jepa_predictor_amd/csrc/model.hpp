@@ -34,17 +34,24 @@ struct LayerW {
 };
 
 // Per-plan-shape device state: inputs copied in, per-round history out.
+// Device state of the plan path, for `batch` independent problems planned together
+// (one predictor batch of batch * n candidates).  Per round rd: samples
+// x_hist[rd][b n + i][ha], energies e_hist[rd][b n + i], elites elites[rd][b][k];
+// Gaussians mu_hist[rd][b][ha] (round 0 = the caller's); per problem z_obs,
+// z_goal, s0 and the frame-0 tokens f0.
 struct PlanState {
-  int n = 0, k = 0, r = 0, h = 0, ha = 0;
+  int n = 0, k = 0, r = 0, h = 0, ha = 0, batch = 0;   // capacity
   void* mem = nullptr;
   float *x_hist = nullptr, *e_hist = nullptr, *mu_hist = nullptr, *sigma_hist = nullptr;
   int* elites = nullptr;
   float *zobs = nullptr, *zgoal = nullptr, *s0 = nullptr;
+  void *zobs_t = nullptr, *f0 = nullptr;               // model dtype [batch, P, E], [batch, P, d]
   uint32_t* params = nullptr;
-  int last_n = 0, last_k = 0, last_r = 0, last_h = 0;   // shape of the last plan run
+  int last_n = 0, last_k = 0, last_r = 0, last_h = 0, last_batch = 0;   // the last plan run
 };
 
-using GraphKey = std::tuple<int, int, int, int, uint32_t, uint32_t>;
+// n, k, rounds, horizon, clamp bits, batch
+using GraphKey = std::tuple<int, int, int, int, uint32_t, uint32_t, int>;
 
 }  // namespace cem
 
@@ -89,7 +96,9 @@ void model_destroy(cem_model* m);
 
 Status rollout(cem_model* m, const float* actions, int n, int horizon, const float* z_obs,
                const float* s0, void* z_pred, hipStream_t st);
-Status plan(cem_model* m, const cem_params& p, const float* z_obs, const float* z_goal,
+// `batch` independent plan steps in one predictor batch; problem b uses plan id
+// p.plan_id + b and the b-th slice of every per-problem argument.
+Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, const float* z_goal,
             const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
             hipStream_t st);
 Status plan_trace(cem_model* m, int kind, void* dst, size_t bytes, hipStream_t st);

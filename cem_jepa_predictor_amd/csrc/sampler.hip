@@ -58,6 +58,13 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ m
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (4 * c >= total) return;
   if (dev_params) { k0 = dev_params[0]; k1 = dev_params[1]; plan_id = dev_params[2]; }
+  // problem b of a batch: its own Gaussian and sample block, plan id + b
+  const int b = blockIdx.y;
+  plan_id += (uint32_t)b;
+  mu += (long long)b * ha;
+  sigma += (long long)b * ha;
+  x += (long long)b * total;
+  if (raw) raw += (long long)b * total;
   const Words w = philox4x32_10((uint32_t)c, round, plan_id, 0u, k0, k1);
   float z[4];
   box_muller(w.w[0], w.w[1], z[0], z[1]);
@@ -82,11 +89,11 @@ __global__ void set_params_kernel(uint32_t* p, uint32_t k0, uint32_t k1, uint32_
 
 hipError_t launch_sample(const float* mu, const float* sigma, int n, int ha, uint64_t seed,
                          uint32_t round, uint32_t plan_id, const uint32_t* dev_params, float lo,
-                         float hi, float* x, uint32_t* raw, hipStream_t stream) {
+                         float hi, float* x, uint32_t* raw, hipStream_t stream, int batch) {
   const int total = n * ha;
-  if (total <= 0) return hipSuccess;
+  if (total <= 0 || batch <= 0) return hipSuccess;
   const int counters = (total + 3) / 4;
-  const int blocks = (counters + 255) / 256;
+  const dim3 blocks((unsigned)((counters + 255) / 256), (unsigned)batch);
   sample_kernel<<<blocks, 256, 0, stream>>>(mu, sigma, total, ha, (uint32_t)seed,
                                             (uint32_t)(seed >> 32), round, plan_id, dev_params,
                                             lo, hi, x, raw);

@@ -32,6 +32,13 @@ __global__ __launch_bounds__(1024) void select_refit_kernel(const float* __restr
                                                             float* __restrict__ sigma) {
   extern __shared__ uint64_t keys[];
   const int tid = threadIdx.x;
+  {  // problem b of a batch: one workgroup each
+    const int b = blockIdx.x;
+    E += (long long)b * n;
+    if (X) X += (long long)b * n * ha;
+    idx += (long long)b * k;
+    if (mu) { mu += (long long)b * ha; sigma += (long long)b * ha; }
+  }
   for (int i = tid; i < npad; i += blockDim.x) keys[i] = i < n ? select_key(E[i], i) : ~0ull;
   __syncthreads();
   for (int size = 2; size <= npad; size <<= 1) {
@@ -104,11 +111,11 @@ hipError_t select_init() {
 }
 
 hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int ha, int* idx,
-                               float* mu, float* sigma, hipStream_t stream) {
-  if (n <= 0 || k <= 0) return hipSuccess;
+                               float* mu, float* sigma, hipStream_t stream, int batch) {
+  if (n <= 0 || k <= 0 || batch <= 0) return hipSuccess;
   int npad = 2;
   while (npad < n) npad <<= 1;
-  select_refit_kernel<<<1, 1024, npad * sizeof(uint64_t), stream>>>(E, X, n, npad, k, ha, idx, mu,
+  select_refit_kernel<<<batch, 1024, npad * sizeof(uint64_t), stream>>>(E, X, n, npad, k, ha, idx, mu,
                                                                       sigma);
   return hipGetLastError();
 }

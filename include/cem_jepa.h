@@ -120,6 +120,23 @@ cem_status cem_plan(cem_model* model, const cem_params* params, const float* z_o
                     const float* z_goal, const float* s0, float* mu, float* sigma,
                     float* action, int32_t* best_idx, void* stream);
 
+/* Fleet batching (page section 06, "C. Fleet-level batching"): `batch`
+ * independent plan steps -- e.g. one per robot -- searched together, their
+ * candidates packed into one predictor batch per round.  Problem b plans with
+ * plan id params->plan_id + b on its own slice of every per-problem argument:
+ *   z_obs, z_goal : device fp32 [batch, P, E];  s0 : device fp32 [batch, S]
+ *   mu, sigma     : device fp32 [batch, H, A]   in/out as in cem_plan
+ *   action        : device fp32 [batch, A];  best_idx : device int32 [batch]
+ * params->n_samples and n_elites are per problem (batch * n_samples <=
+ * max_samples, batch <= 4096).  Problem b's results equal those of cem_plan
+ * with plan id params->plan_id + b on its own inputs, bit for bit.  The trace
+ * of a batched plan holds every problem: actions [R, batch * N, H, A], energies
+ * [R, batch * N], elites [R, batch, K] (indices within each problem), mu and
+ * sigma [R + 1, batch, H, A]. */
+cem_status cem_plan_batched(cem_model* model, const cem_params* params, int32_t batch,
+                            const float* z_obs, const float* z_goal, const float* s0, float* mu,
+                            float* sigma, float* action, int32_t* best_idx, void* stream);
+
 typedef enum {
   CEM_TRACE_ACTIONS = 0,  /* fp32 [R, N, H, A] sampled candidates */
   CEM_TRACE_ENERGY = 1,   /* fp32 [R, N] energies */

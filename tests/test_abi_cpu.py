@@ -160,3 +160,10 @@ def test_warm_start_validates_before_launch(lib):
     assert lib.cem_warm_start(fake, fake, 2, 7, 0.0, 1.0, -0.5, fake, fake, None) == -1
     assert lib.cem_warm_start(fake, fake, 2, 7, float("inf"), 1.0, 0.0, fake, fake, None) == -1
     assert lib.cem_warm_start(fake, ctypes.c_void_p(0x1002), 2, 7, 0.0, 1.0, 0.0, fake, fake, None) == -1
+
+
+def test_plan_batched_validates_null_model(lib):
+    p = _lib.Params(8, 2, 1, 1, -1.0, 1.0, 0, 0, 1)
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.cem_plan_batched(None, ctypes.byref(p), 2, fake, fake, fake, fake, fake, fake, None,
+                                None) == -1

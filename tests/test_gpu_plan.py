@@ -253,3 +253,74 @@ def test_warm_started_closed_loop_lockstep(gpu_lib, floor):
         np.testing.assert_array_equal(to_np(mt), mu)
         np.testing.assert_array_equal(to_np(st), sigma)
         np.testing.assert_array_equal(mu[0], out["mu_out"][1])
+
+
+def _problems(name, batch):
+    """Per-problem inputs: problem 0 is the workload's own, the others differ in
+    observation, goal, state and starting Gaussian."""
+    wl, _, _, z_obs, z_goal, s0 = workload_data(name)
+    pc, m = wl.plan, wl.model
+    H, A = pc.horizon, m.action_dim
+    rng = np.random.default_rng(17)
+    zo = [z_obs] + [rng.standard_normal(z_obs.shape).astype(np.float32) for _ in range(batch - 1)]
+    zg = [z_goal] + [rng.standard_normal(z_goal.shape).astype(np.float32) for _ in range(batch - 1)]
+    st = [s0] + [rng.uniform(-0.5, 0.5, s0.shape).astype(np.float32) for _ in range(batch - 1)]
+    mu = [np.full((H, A), pc.mu0, np.float32)] + [rng.uniform(-0.3, 0.3, (H, A)).astype(np.float32)
+                                                  for _ in range(batch - 1)]
+    sg = [np.full((H, A), pc.sigma0, np.float32)] + [rng.uniform(0.2, 1.0, (H, A)).astype(np.float32)
+                                                     for _ in range(batch - 1)]
+    return [np.stack(v) for v in (zo, zg, st, mu, sg)]
+
+
+@pytest.mark.parametrize("name,batch,use_graph", [("tiny", 3, True), ("small", 2, True), ("tiny", 2, False)])
+def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
+    """Fleet batching (page section 06 C): a batched plan of several problems in one
+    predictor batch gives each problem exactly its own cem_plan result (plan id
+    + b), trace included."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+
+    wl = workload_data(name)[0]
+    pc, m = wl.plan, wl.model
+    N, K, R, H, A = pc.n_samples, pc.n_elites, min(pc.rounds, 3), pc.horizon, m.action_dim
+    log(f"batched plan {name}: {batch} problems x N={N}, R={R}, graph={use_graph}")
+    zo, zg, st, mu, sg = _problems(name, batch)
+    model = gpu_model(name, batch * N)
+    kw = dict(n_samples=N, n_elites=K, rounds=R, horizon=H, seed=pc.seed, clamp_lo=pc.clamp_lo,
+              clamp_hi=pc.clamp_hi, use_graph=use_graph)
+
+    def traces(nb):
+        f32, i32 = torch.float32, torch.int32
+        return {
+            "x": to_np(model.trace(_lib.TRACE_ACTIONS, torch.empty((R, nb * N, H, A), dtype=f32, device="cuda"))),
+            "e": to_np(model.trace(_lib.TRACE_ENERGY, torch.empty((R, nb * N), dtype=f32, device="cuda"))),
+            "el": to_np(model.trace(_lib.TRACE_ELITES, torch.empty((R, nb, K), dtype=i32, device="cuda"))),
+            "mu": to_np(model.trace(_lib.TRACE_MU, torch.empty((R + 1, nb, H, A), dtype=f32, device="cuda"))),
+            "sg": to_np(model.trace(_lib.TRACE_SIGMA, torch.empty((R + 1, nb, H, A), dtype=f32, device="cuda"))),
+        }
+
+    mu_t, sg_t = to_dev(mu), to_dev(sg)
+    act = torch.empty((batch, A), dtype=torch.float32, device="cuda")
+    best = torch.empty(batch, dtype=torch.int32, device="cuda")
+    model.plan_batched(to_dev(zo), to_dev(zg), to_dev(st), mu_t, sg_t, act, best, plan_id=4, **kw)
+    torch.cuda.synchronize()
+    tb = traces(batch)
+    got = {"act": to_np(act), "mu": to_np(mu_t), "sg": to_np(sg_t), "best": to_np(best)}
+    for b in range(batch):
+        mb, sb = to_dev(mu[b]), to_dev(sg[b])
+        ab = torch.empty(A, dtype=torch.float32, device="cuda")
+        bb = torch.empty(1, dtype=torch.int32, device="cuda")
+        model.plan(to_dev(zo[b]), to_dev(zg[b]), to_dev(st[b]), mb, sb, ab, bb, plan_id=4 + b, **kw)
+        torch.cuda.synchronize()
+        t1 = traces(1)
+        np.testing.assert_array_equal(got["act"][b], to_np(ab), err_msg=f"problem {b} action")
+        np.testing.assert_array_equal(got["mu"][b], to_np(mb))
+        np.testing.assert_array_equal(got["sg"][b], to_np(sb))
+        assert got["best"][b] == int(bb.item())
+        np.testing.assert_array_equal(tb["x"][:, b * N:(b + 1) * N], t1["x"])
+        np.testing.assert_array_equal(tb["e"][:, b * N:(b + 1) * N], t1["e"])
+        np.testing.assert_array_equal(tb["el"][:, b], t1["el"][:, 0])
+        np.testing.assert_array_equal(tb["mu"][:, b], t1["mu"][:, 0])
+        np.testing.assert_array_equal(tb["sg"][:, b], t1["sg"][:, 0])
+    # the problems really differ
+    assert not np.array_equal(tb["e"][:, :N], tb["e"][:, N:2 * N])
