@@ -22,6 +22,13 @@ stated sizes supports) are:
 
 Weights are the same dict the input generator draws; for bf16 models they are
 already bf16-representable, and this module still computes in float64.
+
+fp8 projections (page section 06, "D. Model compression": quantizing the
+predictor shrinks the compute term; the OCP E4M3 format of the gfx950 matrix
+cores): with fp8_projections the two LayerNorm-fed projections (fused q|k|v and
+MLP up) see their weights quantized per tensor and their LayerNorm outputs
+quantized per token row to E4M3 (oracle/fp8.py), then dequantized; every other
+step is unchanged.
 """
 from __future__ import annotations
 
@@ -67,13 +74,33 @@ def attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, allowed: np.ndarray) 
 class Predictor:
     """The predictor with float64 copies of the weights."""
 
-    def __init__(self, weights: Dict[str, np.ndarray], layers: int, heads: int, eps: float):
+    def __init__(self, weights: Dict[str, np.ndarray], layers: int, heads: int, eps: float,
+                 fp8_projections: bool = False):
         self.w = {k: np.asarray(v, dtype=F64) for k, v in weights.items()}
         self.layers = layers
         self.heads = heads
         self.eps = eps
         self.d = self.w["b_in"].shape[0]
         self.dh = self.d // heads
+        self.fp8 = fp8_projections
+        if self.fp8:
+            from .fp8 import dequantize, quantize_tensor
+
+            for l in range(layers):
+                for name in (f"l{l}.w_qkv", f"l{l}.w_1"):
+                    codes, scale = quantize_tensor(np.asarray(weights[name], dtype=np.float32))
+                    self.w[name] = dequantize(codes, scale)
+
+    def _proj_input(self, h: np.ndarray) -> np.ndarray:
+        """Input of a LayerNorm-fed projection: itself, or in fp8 mode its per-row
+        E4M3 quantization (float32 rows), dequantized."""
+        if not self.fp8:
+            return h
+        from .fp8 import dequantize, quantize_rows
+
+        rows = h.reshape(-1, h.shape[-1]).astype(np.float32)
+        codes, scale = quantize_rows(rows)
+        return dequantize(codes, scale[:, None]).reshape(h.shape)
 
     # -- pieces -------------------------------------------------------------
     def embed_block(self, a_t: np.ndarray, s_t: np.ndarray, f_t: np.ndarray) -> np.ndarray:
@@ -94,7 +121,7 @@ class Predictor:
 
     def qkv(self, l: int, x: np.ndarray):
         w = self.w
-        h = layer_norm(x, w[f"l{l}.ln1_g"], w[f"l{l}.ln1_b"], self.eps)
+        h = self._proj_input(layer_norm(x, w[f"l{l}.ln1_g"], w[f"l{l}.ln1_b"], self.eps))
         y = h @ w[f"l{l}.w_qkv"] + w[f"l{l}.b_qkv"]
         d = self.d
         return (self.split_heads(y[..., :d]), self.split_heads(y[..., d:2 * d]),
@@ -103,7 +130,7 @@ class Predictor:
     def attn_out_and_mlp(self, l: int, x: np.ndarray, o_heads: np.ndarray) -> np.ndarray:
         w = self.w
         x = x + self.merge_heads(o_heads) @ w[f"l{l}.w_o"] + w[f"l{l}.b_o"]
-        h = layer_norm(x, w[f"l{l}.ln2_g"], w[f"l{l}.ln2_b"], self.eps)
+        h = self._proj_input(layer_norm(x, w[f"l{l}.ln2_g"], w[f"l{l}.ln2_b"], self.eps))
         u = gelu(h @ w[f"l{l}.w_1"] + w[f"l{l}.b_1"])
         return x + u @ w[f"l{l}.w_2"] + w[f"l{l}.b_2"]
 
