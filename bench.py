@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0   # MI355X dense bf16
 MFMA_F32_PEAK_TFLOPS = 157.3     # MI355X fp32 (reference for fp32 models)
+MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8
 
 # HBM-side bytes per dense-GEMM launch, from two rocprofv3 --pmc passes over
 # `bench.py --steps 1 --warmup 0 --no-cpu-baseline` (FETCH_SIZE, then WRITE_SIZE,
@@ -134,17 +135,19 @@ def plan_roofline_ms(m, pc, peak_tflops: float) -> float:
     """Per-kernel roofline of one plan step: the sum over kernels of
     max(FLOPs / MFMA peak, bytes / HBM peak), each activation read or written once
     per kernel, LayerNorm folded into the projections (no separate pass), KV-cached
-    block-causal attention counted on its unmasked part only."""
-    es = 2 if m.dtype == "bf16" else 4
+    block-causal attention counted on its unmasked part only.  fp8 models: the
+    q|k|v and MLP-up projections at the fp8 peak with 1-byte operands."""
+    es = 4 if m.dtype == "f32" else 2
     peak = peak_tflops * 1e12
     N, R, H = pc.n_samples, pc.rounds, pc.horizon
     B, P, E, d, F, L = m.patches + 2, m.patches, m.enc_dim, m.d_model, m.d_mlp, m.layers
     M = N * B
 
-    def gemm(rows, n, k, residual=False):
+    def gemm(rows, n, k, residual=False, f8=False):
         flop = 2.0 * rows * n * k
-        byts = es * (rows * k + n * k + rows * n * (2 if residual else 1))
-        return max(flop / peak, byts / HBM_PEAK_BYTES_PER_S)
+        ein = 1 if f8 else es
+        byts = ein * (rows * k + n * k) + es * rows * n * (2 if residual else 1)
+        return max(flop / (MFMA_FP8_PEAK_TFLOPS * 1e12 if f8 else peak), byts / HBM_PEAK_BYTES_PER_S)
 
     total = gemm(P, d, E)                                   # frame in-projection, once per plan
     per_round = 0.0
@@ -152,7 +155,9 @@ def plan_roofline_ms(m, pc, peak_tflops: float) -> float:
         if t > 0:
             per_round += gemm(N * P, d, E)                  # in-projection of the fed-back frame
         for _ in range(L):
-            per_round += gemm(M, 3 * d, d) + gemm(M, d, d, True) + gemm(M, F, d) + gemm(M, d, F, True)
+            f8 = m.dtype == "fp8"
+            per_round += (gemm(M, 3 * d, d, f8=f8) + gemm(M, d, d, True) + gemm(M, F, d, f8=f8)
+                          + gemm(M, d, F, True))
             kv = (t + 1) * B
             flop = 4.0 * N * B * kv * d
             byts = es * N * (B * d + 2 * kv * d + B * d)
@@ -370,7 +375,15 @@ def main() -> int:
         eager_ms = ev0.elapsed_time(ev1) / nt
         launches, gemm_ms, flop = model.timer_read()
         model.timer_enable(False)
-        peak = MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        peak = MFMA_F32_PEAK_TFLOPS if m.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS
+        peak_note = None
+        if m.dtype == "fp8":
+            # q|k|v and MLP-up (7 of the 12 d^2 per layer, per token) run at the fp8 peak:
+            # the launches' combined peak weights each kind by its FLOPs
+            f8, b16 = 7.0 * m.d_model * m.d_model, 5.0 * m.d_model * m.d_model
+            peak = round((f8 + b16) / (f8 / MFMA_FP8_PEAK_TFLOPS + b16 / MFMA_BF16_PEAK_TFLOPS), 1)
+            peak_note = ("FLOP-weighted: q|k|v and MLP-up at the fp8 peak 5000, output and MLP-down "
+                         "at the bf16 peak 2500 (frame projections ~1 % of FLOPs, counted as bf16)")
         achieved = flop / (gemm_ms * 1e-3) / 1e12
         traffic = None
         if m.dtype == "bf16" and gemm_sources_sha256() == GEMM_COUNTERS["sources_sha256"]:
@@ -390,10 +403,12 @@ def main() -> int:
                 "frac": round(achieved / peak, 4), "traffic": traffic,
                 "traffic_unit": "HBM-side bytes per launch (rocprofv3 FETCH_SIZE + WRITE_SIZE, "
                                 "copy-calibrated)",
-                "kernel": "gemm_bf16_kernel" if m.dtype == "bf16" else "gemm_f32_kernel",
+                "kernel": "gemm_f32_kernel" if m.dtype == "f32" else "gemm_bf16_kernel",
                 "launches": launches, "avg_launch_ms": round(gemm_ms / max(launches, 1), 4),
                 "gemm_share_of_step": round(gemm_ms / nt / eager_ms, 4),
                 "sustained_mfma_ceiling": ceiling}
+        if peak_note:
+            roof["peak_note"] = peak_note
         eprint(f"[bench] GEMMs: {launches} launches, {gemm_ms / nt:.2f} ms/step, "
                f"{achieved:.1f} TFLOP/s; eager step {eager_ms:.2f} ms")
 
@@ -404,12 +419,13 @@ def main() -> int:
 
     value = NB * N * R / (ms * 1e-3)
     pc_all = dataclasses.replace(pc, n_samples=N * NB)   # a batch rolls out NB * N candidates a round
-    plan_ms_roof = plan_roofline_ms(m, pc_all, MFMA_BF16_PEAK_TFLOPS if m.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS)
+    plan_ms_roof = plan_roofline_ms(m, pc_all, MFMA_F32_PEAK_TFLOPS if m.dtype == "f32" else MFMA_BF16_PEAK_TFLOPS)
     out = {
         "metric": "predictor candidate-evals/sec + ms per CEM plan step (800x10) on 1 MI355X",
         "value": round(value, 2), "unit": "candidate-evals/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": m.dtype,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "fp8 e4m3 (q|k|v, MLP-up) + bf16" if m.dtype == "fp8" else m.dtype,
         "data": "synthetic: random-init weights N(0,0.02) (seed 0), N(0,1) embeddings (seed 1), "
                 "CEM seed 2",
         "config": {"workload": wl.name, "n_samples": N, "n_elites": K, "rounds": R, "horizon": H,

@@ -18,14 +18,15 @@ from .inputs import ModelConfig
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcem_jepa.so")
 
-CEM_F32, CEM_BF16 = 0, 1
+CEM_F32, CEM_BF16, CEM_FP8 = 0, 1, 2
+_MODEL_DTYPES = {"f32": CEM_F32, "bf16": CEM_BF16, "fp8": CEM_FP8}
 TRACE_ACTIONS, TRACE_ENERGY, TRACE_ELITES, TRACE_MU, TRACE_SIGMA = range(5)
 STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYPE",
                 -4: "CEM_E_OOM", -5: "CEM_E_HIP", -6: "CEM_E_INTERNAL"}
 
 EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
            "cem_plan", "cem_plan_batched", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
-           "cem_sample", "topk_select", "cem_warm_start", "cem_timer_enable", "cem_timer_read",
+           "cem_sample", "topk_select", "cem_warm_start", "cem_fp8_quantize_rows", "cem_timer_enable", "cem_timer_read",
            "cem_mfma_ceiling"]
 
 
@@ -87,6 +88,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cem_sample": [P, P, I32, I32, I32, U64, U32, U32, F32, F32, P, P, P],
         "topk_select": [P, I32, I32, P, P],
         "cem_warm_start": [P, P, I32, I32, F32, F32, F32, P, P, P],
+        "cem_fp8_quantize_rows": [P, I32, I32, P, P, P],
         "cem_timer_enable": [P, I32],
         "cem_timer_read": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)],
@@ -198,7 +200,7 @@ class _OnStream:
 def model_desc(m: ModelConfig, max_samples: int, max_horizon: Optional[int] = None) -> ModelDesc:
     return ModelDesc(m.layers, m.d_model, m.heads, m.d_mlp, m.patches, m.enc_dim, m.action_dim,
                      m.state_dim, max_horizon or m.max_horizon, max_samples,
-                     CEM_BF16 if m.dtype == "bf16" else CEM_F32, m.ln_eps)
+                     _MODEL_DTYPES[m.dtype], m.ln_eps)
 
 
 def weights_count(desc: ModelDesc) -> int:
@@ -284,7 +286,7 @@ class Model:
         if actions.dim() != 3:
             raise ValueError(f"actions: expected [n, h, {c.action_dim}], got {tuple(actions.shape)}")
         n, h = actions.shape[0], actions.shape[1]
-        zdt = torch.bfloat16 if c.dtype == "bf16" else torch.float32
+        zdt = torch.float32 if c.dtype == "f32" else torch.bfloat16
         ptrs = _args((actions, "actions", _f32(), (n, h, c.action_dim)),
                      (z_obs, "z_obs", _f32(), (c.patches, c.enc_dim)),
                      (s0, "s0", _f32(), (c.state_dim,)),
@@ -366,6 +368,18 @@ def warm_start(mu_prev, sigma_prev, mu_fill, sigma_fill, sigma_floor, mu_next, s
     with _OnStream(stream) as st:
         _check(load().cem_warm_start(ptrs[0], ptrs[1], h, a, mu_fill, sigma_fill, sigma_floor,
                                      ptrs[2], ptrs[3], st))
+
+
+def fp8_quantize_rows(x, codes, scale, stream=None):
+    """Per-row OCP e4m3 quantization of fp32 rows (cem_fp8_quantize_rows)."""
+    import torch
+
+    if x.dim() != 2:
+        raise ValueError(f"x: expected [rows, cols], got {tuple(x.shape)}")
+    r, c = x.shape
+    ptrs = _args((x, "x", _f32()), (codes, "codes", (torch.uint8,), (r, c)), (scale, "scale", _f32(), (r,)))
+    with _OnStream(stream) as st:
+        _check(load().cem_fp8_quantize_rows(ptrs[0], r, c, ptrs[1], ptrs[2], st))
 
 
 def mfma_ceiling(random_operands: bool = True, launches: int = 40):

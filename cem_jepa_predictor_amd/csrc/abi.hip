@@ -232,6 +232,18 @@ cem_status cem_warm_start(const float* mu_prev, const float* sigma_prev, int32_t
   });
 }
 
+cem_status cem_fp8_quantize_rows(const float* x, int32_t rows, int32_t cols, uint8_t* codes,
+                                 float* scale, void* stream) {
+  return guarded([&]() -> cem_status {
+    if (!x || !codes || !scale) return fail(CEM_E_ARG, "null argument");
+    if (!aligned(x, 4) || !aligned(codes, 8) || !aligned(scale, 4)) return fail(CEM_E_ARG, "misaligned pointer");
+    if (rows < 0 || cols < 8 || cols % 8 != 0 || (long long)rows * cols > (1LL << 31))
+      return fail(CEM_E_SHAPE, "need rows >= 0, cols a positive multiple of 8, rows * cols <= 2^31");
+    return check_hip(cem::launch_quantize_rows_fp8(x, rows, cols, codes, scale, static_cast<hipStream_t>(stream)),
+                     "fp8 quantize kernel");
+  });
+}
+
 cem_status topk_select(const float* energy, int32_t n, int32_t k, int32_t* idx, void* stream) {
   return guarded([&]() -> cem_status {
     if (!energy || !idx) return fail(CEM_E_ARG, "null argument");

@@ -69,6 +69,27 @@ struct Epilogue {
 
 enum class Act { None, Gelu };
 
+// OCP e4m3 quantization of one row (the format of gfx950's 8-bit matrix-core
+// operands): scale = amax / 448, codes = e4m3(clamp(v * (448 / amax), +-448)),
+// rounded to nearest even by the hardware conversion; an all-zero row gets scale 1.
+__device__ __forceinline__ void fp8_row_scale(float amax, float& inv, float& scale) {
+  const bool zero = !(amax > 0.f);
+  const float safe = zero ? 448.0f : amax;
+  inv = 448.0f / safe;
+  scale = zero ? 1.0f : safe / 448.0f;
+}
+// eight values -> eight codes (little-endian in a uint2)
+__device__ __forceinline__ uint2 fp8x8(const float v[8], float inv) {
+  float c[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) c[i] = fminf(fmaxf(v[i] * inv, -448.0f), 448.0f);
+  int lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[0], c[1], 0, false);
+  lo = __builtin_amdgcn_cvt_pk_fp8_f32(c[2], c[3], lo, true);
+  int hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[4], c[5], 0, false);
+  hi = __builtin_amdgcn_cvt_pk_fp8_f32(c[6], c[7], hi, true);
+  return make_uint2((uint32_t)lo, (uint32_t)hi);
+}
+
 // GELU(x) = x * Phi(x) with Phi from the exact erf (libm erff): fp32 models.
 __device__ __forceinline__ float gelu_exact(float x) {
   return 0.5f * x * (1.0f + erff(x * 0.70710678118654752440f));

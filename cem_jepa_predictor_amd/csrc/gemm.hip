@@ -48,6 +48,13 @@
 //    never reads them back).
 //  * One kernel instantiation per epilogue kind (plain, GELU, residual), so
 //    each carries only its own epilogue code.
+//  * fp8 operands (OCP e4m3 codes, the gfx950 matrix cores' 8-bit format):
+//    the same ring of 128-byte rows then holds 128 k-values per slab, each
+//    slab is two substeps of v_mfma_f32_32x32x64_f8f6f4, and A fragments are
+//    reloaded in place right after their last use (two fragment sets would not
+//    fit the register budget of two waves per SIMD).  Row scales of A and one
+//    scale for all of B are applied in the epilogue; the bias enters the
+//    accumulators divided by both.  Plain and GELU epilogues.
 //
 // Epilogue (fp32): + bias (preloaded into the accumulators), optional GELU,
 // optional residual add (the output already holds the residual stream),
@@ -114,6 +121,7 @@ __device__ __forceinline__ void epilogue_row4(const Epilogue& e, int N, long lon
 
 // ------------------------------------------------------------------ bf16 MFMA kernel
 constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
+constexpr int BK8 = 128;                    // fp8 operands: k-values per 128-byte LDS row
 constexpr int NE = 5;                       // entries in the operand ring
 constexpr int ENT = BM * BK * 2;            // 32 KB: one operand slab (256 rows x 128 B)
 constexpr int GROUP_M = 8;
@@ -124,24 +132,37 @@ struct TileCoord {
   int m0, n0, rows_a, rows_b;   // rows_a = rows_b = 0: no tile (loads read zeros)
 };
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const bf16* base, int row0, int rows,
+// A buffer resource over rows row0 .. row0 + rows - 1 of a row-major operand
+// (ld elements of ES bytes), starting at column k: loads beyond it read zeros.
+template <int ES>
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, int row0, int rows,
                                                             int ld, int k) {
-  const uint32_t bytes = (uint32_t)rows * (uint32_t)ld * 2u - (uint32_t)k * 2u;
+  const uint32_t bytes = ((uint32_t)rows * (uint32_t)ld - (uint32_t)k) * (uint32_t)ES;
   return __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<bf16*>(base + (long long)row0 * ld + k), (short)0, (int)bytes, 0x00020000);
+      const_cast<uint8_t*>(static_cast<const uint8_t*>(base) + ((long long)row0 * ld + k) * ES),
+      (short)0, (int)bytes, 0x00020000);
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-template <int KIND>
-__global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict__ A, int lda,
-                                                         const bf16* __restrict__ Bt, int ldb,
-                                                         int M, int N, int K, Epilogue epi) {
+// F8: operands are OCP fp8 e4m3 codes; A row m is scaled by row_scale[m] and all of
+// Bt by w_scale, so out = row_scale[m] w_scale (A Bt^T)[m, n] + bias[n].  The bias
+// enters the accumulators divided by both scales (epi.bias holds bias / w_scale).
+template <int KIND, bool F8>
+__global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict__ A, int lda,
+                                                         const void* __restrict__ Bt, int ldb,
+                                                         int M, int N, int K, Epilogue epi,
+                                                         const float* __restrict__ row_scale,
+                                                         float w_scale) {
+  static_assert(!(F8 && KIND == kEpiResidual), "fp8 operands feed the plain and GELU epilogues only");
+  constexpr int ES = F8 ? 1 : 2;             // operand bytes per element
+  constexpr int KS = F8 ? BK8 : BK;          // k-values per slab
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NE * ENT];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN, tiles = tiles_m * tiles_n;
-  const int KT = K / BK;
+  const int KT = K / KS;
 
   // This workgroup's tiles.  The dispatcher hands workgroup b to XCD b % 8; XCD x
   // owns a contiguous range of logical tiles (groups of 8 row-tiles sharing A and
@@ -178,18 +199,18 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int dlrow = 32 * wave + (lane >> 3);
   const int dpos = lane & 7, dsw = (lane >> 4) & 3;
   const int dc0 = dpos ^ dsw, dc1 = dpos ^ (dsw | 4);           // d even / odd
-  const int va0 = dlrow * lda * 2 + (dc0 << 4), va1 = dlrow * lda * 2 + (dc1 << 4);
-  const int vb0 = dlrow * ldb * 2 + (dc0 << 4), vb1 = dlrow * ldb * 2 + (dc1 << 4);
+  const int va0 = dlrow * lda * ES + (dc0 << 4), va1 = dlrow * lda * ES + (dc1 << 4);
+  const int vb0 = dlrow * ldb * ES + (dc0 << 4), vb1 = dlrow * ldb * ES + (dc1 << 4);
   auto dma_a = [&](const TileCoord& t, int kt, int entry, int d) {
-    const int kb = kt * BK;
-    const __amdgpu_buffer_rsrc_t r = slab_rsrc(A, t.m0, t.rows_a, lda, t.rows_a ? kb : 0);
-    const int v = ((d & 1) ? va1 : va0) + d * 16 * lda;
+    const int kb = kt * KS;
+    const __amdgpu_buffer_rsrc_t r = slab_rsrc<ES>(A, t.m0, t.rows_a, lda, t.rows_a ? kb : 0);
+    const int v = ((d & 1) ? va1 : va0) + d * 8 * lda * ES;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds + entry * ENT + wave * 4096 + d * 1024), 16, v, 0, 0, 0);
   };
   auto dma_b = [&](const TileCoord& t, int kt, int entry, int d) {
-    const int kb = kt * BK;
-    const __amdgpu_buffer_rsrc_t r = slab_rsrc(Bt, t.n0, t.rows_b, ldb, t.rows_b ? kb : 0);
-    const int v = ((d & 1) ? vb1 : vb0) + d * 16 * ldb;
+    const int kb = kt * KS;
+    const __amdgpu_buffer_rsrc_t r = slab_rsrc<ES>(Bt, t.n0, t.rows_b, ldb, t.rows_b ? kb : 0);
+    const int v = ((d & 1) ? vb1 : vb0) + d * 8 * ldb * ES;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)(lds + entry * ENT + wave * 4096 + d * 1024), 16, v, 0, 0, 0);
   };
 
@@ -204,6 +225,25 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   const int fsw = (fr >> 1) & 7;
   f32x16_t acc[4][2];
   bf16x8_t fa[2][4], fb[2][2];
+  // fp8: v_mfma_f32_32x32x64_f8f6f4, lane l holding 32 k-values 32 (l / 32) ..
+  // of its row: chunks 4 s + 2 (l / 32) and the next of substep s (two per slab).
+  // A fragments are reloaded in place right after their last use; B has two sets.
+  i32x8_t ga[4], gb[2][2];
+  auto frag8 = [&](const uint8_t* p, int s) -> i32x8_t {
+    const int c0 = 4 * s + 2 * fk;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p + ((c0 ^ fsw) << 4));
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + (((c0 + 1) ^ fsw) << 4));
+    return i32x8_t{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w, (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
+  };
+  auto frag8a = [&](int ea, int s, int i) { ga[i] = frag8(lds + ea * ENT + arow + i * 4096, s); };
+  auto frag8b = [&](int ea, int s, int buf, int j) {
+    const int eb = (ea + 1 == NE) ? 0 : ea + 1;
+    gb[buf][j] = frag8(lds + eb * ENT + brow + j * 4096, s);
+  };
+  auto mfma8 = [&](int buf, int i, int j) {
+    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[buf][j], ga[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+  };
+  float rsc[4] = {1.f, 1.f, 1.f, 1.f};   // fp8: row_scale of the lane's row in each 32-row block
   auto frag1 = [&](int ea, int s, int buf, int r) {
     const int pc = ((2 * s + fk) ^ fsw) << 4;
     if (r < 4) {
@@ -219,9 +259,20 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
     const int i = idx >> 1, j = idx & 1;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
   };
-  // accumulators start at the bias (lane quads are 4 consecutive output columns)
+  // accumulators start at the bias (lane quads are 4 consecutive output columns);
+  // fp8: at bias / (row_scale w_scale), and the lane's row scales are kept
   auto init_acc = [&](const TileCoord& t) {
     const int cb = t.n0 + wn * 64 + 4 * fk;
+    float inv[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (F8) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = t.m0 + wm * 128 + 32 * i + fr;
+        rsc[i] = (m < M) ? row_scale[m] : 1.f;
+        inv[i] = __builtin_amdgcn_rcpf(rsc[i]);
+        rsc[i] *= w_scale;
+      }
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -231,8 +282,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
         if (epi.bias && c < N) bb = *reinterpret_cast<const float4*>(epi.bias + c);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          acc[i][j][4 * q] = bb.x; acc[i][j][4 * q + 1] = bb.y;
-          acc[i][j][4 * q + 2] = bb.z; acc[i][j][4 * q + 3] = bb.w;
+          acc[i][j][4 * q] = bb.x * inv[i]; acc[i][j][4 * q + 1] = bb.y * inv[i];
+          acc[i][j][4 * q + 2] = bb.z * inv[i]; acc[i][j][4 * q + 3] = bb.w * inv[i];
         }
       }
   };
@@ -262,8 +313,15 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
   CEM_WAIT(8);   // slab 0 landed (this wave's part)
   __builtin_amdgcn_s_barrier();
   F;
+  if constexpr (F8) {
 #pragma unroll
-  for (int r = 0; r < 6; ++r) frag1(0, 0, 0, r);
+    for (int j = 0; j < 2; ++j) frag8b(0, 0, 0, j);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) frag8a(0, 0, i);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 6; ++r) frag1(0, 0, 0, r);
+  }
   F;
   // The slab sequence runs on across tiles: slab KT + j is the next tile's slab j.
   // Slab s: substep 0 loads A of slab s + 2 into the entry that slab s - 1's B
@@ -281,6 +339,31 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       const int ea_n = (eb + 1 == NE) ? 0 : eb + 1;
       const int ea_p = (ea == 0) ? NE - 1 : ea - 1;   // slab s - 1's B entry
       const TileCoord Tt = tile_at(toff);
+      if constexpr (F8) {
+      // fp8 substep 0: B of substep 1 first, each A fragment reloaded after its last
+      // use; A of slab s + 2
+      mfma8(0, 0, 0); F; frag8b(ea, 1, 1, 0); F;
+      mfma8(0, 0, 1); F; frag8b(ea, 1, 1, 1); F; frag8a(ea, 1, 0); F;
+      mfma8(0, 1, 0); F; dma_a(Tt, tkt, ea_p, 0); F;
+      mfma8(0, 1, 1); F; frag8a(ea, 1, 1); F; dma_a(Tt, tkt, ea_p, 1); F;
+      mfma8(0, 2, 0); F; dma_a(Tt, tkt, ea_p, 2); F;
+      mfma8(0, 2, 1); F; frag8a(ea, 1, 2); F; dma_a(Tt, tkt, ea_p, 3); F;
+      mfma8(0, 3, 0); F;
+      mfma8(0, 3, 1); F; frag8a(ea, 1, 3); F;
+      // slab s + 1 landed (every load but the last 4: A of slab s + 2), own reads done
+      CEM_WAIT(4);
+      __builtin_amdgcn_s_barrier();
+      F;
+      // fp8 substep 1: slab s + 1's first fragments; B of slab s + 2
+      mfma8(1, 0, 0); F; frag8b(ea_n, 0, 0, 0); F;
+      mfma8(1, 0, 1); F; frag8b(ea_n, 0, 0, 1); F; frag8a(ea_n, 0, 0); F;
+      mfma8(1, 1, 0); F; dma_b(Tt, tkt, ea, 0); F;
+      mfma8(1, 1, 1); F; frag8a(ea_n, 0, 1); F; dma_b(Tt, tkt, ea, 1); F;
+      mfma8(1, 2, 0); F; dma_b(Tt, tkt, ea, 2); F;
+      mfma8(1, 2, 1); F; frag8a(ea_n, 0, 2); F; dma_b(Tt, tkt, ea, 3); F;
+      mfma8(1, 3, 0); F;
+      mfma8(1, 3, 1); F; frag8a(ea_n, 0, 3); F;
+      } else {
       // substep 0
       mfma1(0, 0); F; frag1(ea, 1, 1, 0); F; frag1(ea, 1, 1, 1); F;
       mfma1(0, 1); F; frag1(ea, 1, 1, 2); F; frag1(ea, 1, 1, 3); F;
@@ -321,6 +404,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
       mfma1(1, 6); F;
       dma_b(Tt, tkt, ea, 3); F;
       mfma1(1, 7); F;
+      }
       if (++tkt == KT) { tkt = 0; ++toff; }
       stage_ep = eb;
       ea = ea_n;
@@ -417,6 +501,10 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
             for (int q = 0; q < 4; ++q) {
               float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                             acc[i][j][4 * q + 3]};
+              if constexpr (F8) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) v[e] *= rsc[i];
+              }
               if constexpr (KIND == kEpiGelu) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] = gelu_bf16_path(v[e]);
@@ -456,6 +544,10 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const bf16* __restrict_
           for (int q = 0; q < 4; ++q) {
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                           acc[i][j][4 * q + 3]};
+            if constexpr (F8) {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] *= rsc[i];
+            }
             epilogue_row4<bf16, KIND>(e_nb, N, row, ncol + j * 32 + 8 * q, v);
           }
       }
@@ -559,14 +651,31 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
   const int grid = tiles < cus ? tiles : cus;   // persistent: one workgroup per CU
   switch (epi_kind(epi)) {
     case kEpiGelu:
-      gemm_bf16_kernel<kEpiGelu><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      gemm_bf16_kernel<kEpiGelu, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 1.f);
       break;
     case kEpiResidual:
-      gemm_bf16_kernel<kEpiResidual><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      gemm_bf16_kernel<kEpiResidual, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 1.f);
       break;
     default:
-      gemm_bf16_kernel<kEpiPlain><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi);
+      gemm_bf16_kernel<kEpiPlain, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 1.f);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8(const uint8_t* A, int lda, const uint8_t* Bt, int ldb, int M, int N, int K,
+                           const float* row_scale, float w_scale, const Epilogue& epi,
+                           hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K <= 0 || K % BK8 != 0 || !row_scale || epi.residual) return hipErrorInvalidValue;
+  int cus = 0;
+  const hipError_t ce = cu_count(&cus);
+  if (ce != hipSuccess) return ce;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int grid = tiles < cus ? tiles : cus;
+  if (epi.gelu)
+    gemm_bf16_kernel<kEpiGelu, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_scale, w_scale);
+  else
+    gemm_bf16_kernel<kEpiPlain, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_scale, w_scale);
   return hipGetLastError();
 }
 

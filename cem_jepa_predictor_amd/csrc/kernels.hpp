@@ -42,6 +42,14 @@ template <typename T>
 hipError_t launch_layernorm(const T* x, int rows, int d, RowMap in_rows, const float* g,
                             const float* b, float eps, T* y, hipStream_t stream);
 bool layernorm_supports(int d);
+// fp8 output (d % 512 == 0): y8[r] = OCP e4m3 codes of LayerNorm(x[in_rows(r)]) scaled
+// by 448 / (its largest magnitude), row_scale[r] = that magnitude / 448 (1 for a zero row).
+hipError_t launch_layernorm_fp8(const bf16* x, int rows, int d, RowMap in_rows, const float* g,
+                                const float* b, float eps, uint8_t* y8, float* row_scale,
+                                hipStream_t stream);
+// The same per-row quantization of fp32 rows [rows, cols] (cols % 8 == 0).
+hipError_t launch_quantize_rows_fp8(const float* x, int rows, int cols, uint8_t* y8,
+                                    float* row_scale, hipStream_t stream);
 
 // --- gemm.hip ----------------------------------------------------------------
 // out = epilogue(A[M, K] @ Bt[N, K]^T); N % 4 == 0; bf16 (MFMA): K % 64 == 0
@@ -50,6 +58,12 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
                             int K, const Epilogue& epi, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N,
                            int K, const Epilogue& epi, hipStream_t stream);
+// fp8 operands (OCP e4m3 codes): out = epilogue(row_scale[m] * w_scale * (A Bt^T)[m, n]
+// + bias[n]) with epi.bias holding bias / w_scale; plain or GELU epilogue only;
+// K % 128 == 0 (hipErrorInvalidValue otherwise).
+hipError_t launch_gemm_fp8(const uint8_t* A, int lda, const uint8_t* Bt, int ldb, int M, int N,
+                           int K, const float* row_scale, float w_scale, const Epilogue& epi,
+                           hipStream_t stream);
 hipError_t gemm_init();   // caches the current device's CU count (persistent grid size)
 
 // --- attention.hip -------------------------------------------------------------

@@ -126,6 +126,93 @@ __global__ __launch_bounds__(256) void layernorm_bf16x8_kernel(const bf16* __res
   }
 }
 
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// LayerNorm of bf16 rows (d = 512 * NC, one wave per row, 8 consecutive values per
+// lane run) with OCP e4m3 output, scaled per row by 448 / amax of the normalised row.
+template <int NC>
+__global__ __launch_bounds__(256) void layernorm_fp8_kernel(const bf16* __restrict__ x, int rows,
+                                                            RowMap in_rows,
+                                                            const float* __restrict__ g,
+                                                            const float* __restrict__ b, float eps,
+                                                            uint8_t* __restrict__ y8,
+                                                            float* __restrict__ row_scale) {
+  constexpr int d = 512 * NC;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const uint4* src = reinterpret_cast<const uint4*>(x + in_rows(r) * (long long)d);
+  float v[8 * NC];
+  float s = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const uint4 u = src[c * 64 + lane];
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+      v[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+      s += v[8 * c + 2 * k] + v[8 * c + 2 * k + 1];
+    }
+  }
+  const float mean = wave_sum(s) * (1.0f / d);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8 * NC; ++i) {
+    const float t = v[i] - mean;
+    q += t * t;
+  }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / d) + eps);
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  const float4* b4 = reinterpret_cast<const float4*>(b);
+  float amax = 0.f;
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const float4 g0 = g4[(c * 64 + lane) * 2], g1 = g4[(c * 64 + lane) * 2 + 1];
+    const float4 b0 = b4[(c * 64 + lane) * 2], b1 = b4[(c * 64 + lane) * 2 + 1];
+    const float gg[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+    const float bb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      v[8 * c + k] = (v[8 * c + k] - mean) * rstd * gg[k] + bb[k];
+      amax = fmaxf(amax, fabsf(v[8 * c + k]));
+    }
+  }
+  float inv, scale;
+  fp8_row_scale(wave_max(amax), inv, scale);
+  uint2* dst = reinterpret_cast<uint2*>(y8 + (long long)r * d);
+#pragma unroll
+  for (int c = 0; c < NC; ++c) dst[c * 64 + lane] = fp8x8(v + 8 * c, inv);
+  if (lane == 0) row_scale[r] = scale;
+}
+
+// Per-row e4m3 quantization of fp32 rows [rows, cols], cols % 8 == 0: one wave per row.
+__global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const float* __restrict__ x, int rows,
+                                                                int cols, uint8_t* __restrict__ y8,
+                                                                float* __restrict__ row_scale) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  const float* xr = x + (long long)r * cols;
+  float amax = 0.f;
+  for (int c = lane * 8; c < cols; c += 512)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) amax = fmaxf(amax, fabsf(xr[c + k]));
+  float inv, scale;
+  fp8_row_scale(wave_max(amax), inv, scale);
+  for (int c = lane * 8; c < cols; c += 512) {
+    float v[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) v[k] = xr[c + k];
+    *reinterpret_cast<uint2*>(y8 + (long long)r * cols + c) = fp8x8(v, inv);
+  }
+  if (lane == 0) row_scale[r] = scale;
+}
+
 template <int NCH, typename T>
 hipError_t run(const T* x, int rows, RowMap in_rows, const float* g, const float* b, float eps,
                T* y, hipStream_t stream) {
@@ -175,6 +262,30 @@ hipError_t launch_layernorm(const T* x, int rows, int d, RowMap in_rows, const f
     case 4096: return run<32>(x, rows, in_rows, g, b, eps, y, stream);
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_layernorm_fp8(const bf16* x, int rows, int d, RowMap in_rows, const float* g,
+                                const float* b, float eps, uint8_t* y8, float* row_scale,
+                                hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int grid = (rows + 3) / 4;
+  switch (d) {
+    case 512: layernorm_fp8_kernel<1><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y8, row_scale); break;
+    case 1024: layernorm_fp8_kernel<2><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y8, row_scale); break;
+    case 1536: layernorm_fp8_kernel<3><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y8, row_scale); break;
+    case 2048: layernorm_fp8_kernel<4><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y8, row_scale); break;
+    case 4096: layernorm_fp8_kernel<8><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y8, row_scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_rows_fp8(const float* x, int rows, int cols, uint8_t* y8,
+                                    float* row_scale, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (cols <= 0 || cols % 8 != 0) return hipErrorInvalidValue;
+  quantize_rows_fp8_kernel<<<(rows + 3) / 4, 256, 0, stream>>>(x, rows, cols, y8, row_scale);
+  return hipGetLastError();
 }
 
 template hipError_t launch_layernorm<float>(const float*, int, int, RowMap, const float*,

@@ -57,6 +57,21 @@ uint16_t host_bf16(float f) {   // round to nearest even (finite inputs)
 
 size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
+// OCP e4m3 code of a finite float with |v| <= 448, rounded to nearest, ties to the
+// even mantissa: 1 sign, 4 exponent (bias 7), 3 mantissa bits; subnormals below 2^-6.
+uint8_t host_e4m3(float v) {
+  const uint8_t sign = std::signbit(v) ? 0x80 : 0x00;
+  const double a = std::fabs((double)v);
+  if (a == 0.0) return sign;
+  int ex = 0;
+  std::frexp(a, &ex);                         // a in [2^(ex-1), 2^ex)
+  int e = std::max(ex - 1, -6);
+  double m = std::nearbyint(std::ldexp(a, -(e - 3)));   // round half to even (default mode)
+  if (m >= 16.0) { m = 8.0; ++e; }
+  if (m < 8.0) return (uint8_t)(sign | (uint8_t)m);     // subnormal (e == -6)
+  return (uint8_t)(sign | (uint8_t)(((e + 7) << 3) | ((int)m - 8)));
+}
+
 // Bump layout over one allocation.
 struct Layout {
   size_t off = 0;
@@ -77,7 +92,10 @@ size_t weights_count(const cem_model_desc& d) {
 
 Status validate_desc(const cem_model_desc& d) {
   auto bad = [](cem_status c, const std::string& m) { Status s; s.code = c; s.msg = m; return s; };
-  if (d.dtype != CEM_F32 && d.dtype != CEM_BF16) return bad(CEM_E_DTYPE, "dtype must be CEM_F32 or CEM_BF16");
+  if (d.dtype != CEM_F32 && d.dtype != CEM_BF16 && d.dtype != CEM_FP8)
+    return bad(CEM_E_DTYPE, "dtype must be CEM_F32, CEM_BF16 or CEM_FP8");
+  if (d.dtype == CEM_FP8 && d.d_model % 512 != 0)
+    return bad(CEM_E_SHAPE, "fp8 models need d_model % 512 == 0");
   if (d.layers < 1 || d.layers > 256) return bad(CEM_E_SHAPE, "layers must be in [1, 256]");
   if (d.heads < 1 || d.d_model < 1 || d.d_model % d.heads != 0)
     return bad(CEM_E_SHAPE, "d_model must be a positive multiple of heads");
@@ -94,7 +112,7 @@ Status validate_desc(const cem_model_desc& d) {
   if (d.max_samples < 1 || d.max_samples > kMaxSelect) return bad(CEM_E_SHAPE, "max_samples must be in [1, 16384]");
   if (!(d.ln_eps > 0.f) || !std::isfinite(d.ln_eps)) return bad(CEM_E_ARG, "ln_eps must be positive and finite");
   const int dh = d.d_model / d.heads, B = d.patches + 2;
-  if (d.dtype == CEM_BF16 && !attention_bf16_supports(dh, B))
+  if (d.dtype != CEM_F32 && !attention_bf16_supports(dh, B))
     return bad(CEM_E_SHAPE, "bf16 attention needs head dim 64 and patches + 2 <= 320");
   if (d.dtype == CEM_F32 && !attention_f32_supports(dh))
     return bad(CEM_E_SHAPE, "fp32 attention needs head dim 16, 32, 64 or 128");
@@ -117,7 +135,8 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   cem_model* m = new cem_model();
   m->desc = d;
   m->device = device;
-  m->bf16 = d.dtype == CEM_BF16;
+  m->bf16 = d.dtype != CEM_F32;
+  m->fp8 = d.dtype == CEM_FP8;
   m->esz = m->bf16 ? 2 : 4;
   m->B = d.patches + 2;
   m->rows_max = (long long)d.max_samples * m->B;
@@ -134,10 +153,11 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   std::vector<LO> lo(L);
   for (size_t l = 0; l < L; ++l) {
     lo[l].ln1_g = wl.take(D * 4); lo[l].ln1_b = wl.take(D * 4);
-    lo[l].w_qkv = wl.take(3 * D * D * es); lo[l].b_qkv = wl.take(3 * D * 4);
+    const size_t es8 = m->fp8 ? 1 : es;   // fp8 models: e4m3 codes for q|k|v and MLP up
+    lo[l].w_qkv = wl.take(3 * D * D * es8); lo[l].b_qkv = wl.take(3 * D * 4);
     lo[l].w_o = wl.take(D * D * es); lo[l].b_o = wl.take(D * 4);
     lo[l].ln2_g = wl.take(D * 4); lo[l].ln2_b = wl.take(D * 4);
-    lo[l].w_1 = wl.take(F * D * es); lo[l].b_1 = wl.take(F * 4);
+    lo[l].w_1 = wl.take(F * D * es8); lo[l].b_1 = wl.take(F * 4);
     lo[l].w_2 = wl.take(D * F * es); lo[l].b_2 = wl.take(D * 4);
   }
   const size_t o_lnf_g = wl.take(D * 4), o_lnf_b = wl.take(D * 4);
@@ -170,15 +190,39 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
       }
     src += in * outd;
   };
+  // fp8: one scale for the whole matrix, ws = amax / 448; codes = e4m3(clamp(v * (448 /
+  // amax), +-448)); the bias that follows is stored divided by ws
+  std::vector<float> ws_qkv(L, 1.f), ws_1(L, 1.f);
+  auto put_mat_t8 = [&](size_t off, size_t in, size_t outd, float& ws) {
+    float amax = 0.f;
+    for (size_t i = 0; i < in * outd; ++i) amax = std::max(amax, std::fabs(src[i]));
+    const float inv = amax > 0.f ? 448.0f / amax : 1.0f;
+    ws = amax > 0.f ? amax / 448.0f : 1.0f;
+    for (size_t i = 0; i < in; ++i)
+      for (size_t o = 0; o < outd; ++o) {
+        const float y = std::min(std::max(src[i * outd + o] * inv, -448.0f), 448.0f);
+        hw[off + o * in + i] = host_e4m3(y);
+      }
+    src += in * outd;
+  };
+  auto put_vec_scaled = [&](size_t off, size_t count, float ws) {
+    for (size_t i = 0; i < count; ++i) {
+      const float v = src[i] / ws;
+      std::memcpy(hw.data() + off + i * 4, &v, 4);
+    }
+    src += count;
+  };
   put_mat_t(o_w_in, E, D); put_vec(o_b_in, D);
   put_vec(o_w_a, A * D); put_vec(o_b_a, D);
   put_vec(o_w_s, S * D); put_vec(o_b_s, D);
   for (size_t l = 0; l < L; ++l) {
     put_vec(lo[l].ln1_g, D); put_vec(lo[l].ln1_b, D);
-    put_mat_t(lo[l].w_qkv, D, 3 * D); put_vec(lo[l].b_qkv, 3 * D);
+    if (m->fp8) { put_mat_t8(lo[l].w_qkv, D, 3 * D, ws_qkv[l]); put_vec_scaled(lo[l].b_qkv, 3 * D, ws_qkv[l]); }
+    else { put_mat_t(lo[l].w_qkv, D, 3 * D); put_vec(lo[l].b_qkv, 3 * D); }
     put_mat_t(lo[l].w_o, D, D); put_vec(lo[l].b_o, D);
     put_vec(lo[l].ln2_g, D); put_vec(lo[l].ln2_b, D);
-    put_mat_t(lo[l].w_1, D, F); put_vec(lo[l].b_1, F);
+    if (m->fp8) { put_mat_t8(lo[l].w_1, D, F, ws_1[l]); put_vec_scaled(lo[l].b_1, F, ws_1[l]); }
+    else { put_mat_t(lo[l].w_1, D, F); put_vec(lo[l].b_1, F); }
     put_mat_t(lo[l].w_2, F, D); put_vec(lo[l].b_2, D);
   }
   put_vec(o_lnf_g, D); put_vec(o_lnf_b, D);
@@ -202,6 +246,7 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
     w.ln2_g = (float*)(wb + lo[l].ln2_g); w.ln2_b = (float*)(wb + lo[l].ln2_b);
     w.w_1_t = wb + lo[l].w_1; w.b_1 = (float*)(wb + lo[l].b_1);
     w.w_2_t = wb + lo[l].w_2; w.b_2 = (float*)(wb + lo[l].b_2);
+    w.ws_qkv = ws_qkv[l]; w.ws_1 = ws_1[l];
   }
   m->lnf_g = (float*)(wb + o_lnf_g); m->lnf_b = (float*)(wb + o_lnf_b);
   m->w_out_t = wb + o_w_out; m->b_out = (float*)(wb + o_b_out);
@@ -215,11 +260,13 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   const size_t o_kv = al.take(kv_slots * rows * 2 * D * es);
   const size_t o_zhat = al.take((size_t)d.max_samples * P * E * es);
   const size_t o_f0 = al.take(P * D * es), o_zobs = al.take(P * E * es);
+  const size_t o_h8 = al.take(m->fp8 ? rows * D : 0), o_hs = al.take(m->fp8 ? rows * 4 : 0);
   e = hipMalloc(&m->arena, al.off);
   if (e != hipSuccess) return fail(hip_status(e, "hipMalloc(workspace)"));
   uint8_t* ab = static_cast<uint8_t*>(m->arena);
   m->x = ab + o_x; m->h = ab + o_h; m->q = ab + o_q; m->u = ab + o_u; m->kv = ab + o_kv;
   m->zhat = ab + o_zhat; m->f0 = ab + o_f0; m->zobs_t = ab + o_zobs;
+  if (m->fp8) { m->h8 = ab + o_h8; m->hs = reinterpret_cast<float*>(ab + o_hs); }
 
   e = select_init();
   if (e != hipSuccess) return fail(hip_status(e, "select_init"));
@@ -280,6 +327,15 @@ hipError_t gemm(cem_model* m, const void* A, int lda, const void* Bt, int ldb, i
   return timer_stop(m, st);
 }
 
+hipError_t gemm8(cem_model* m, const uint8_t* A, int lda, const void* Bt, int ldb, int M, int N,
+                 int K, const float* row_scale, float w_scale, const Epilogue& e, hipStream_t st) {
+  hipError_t r = timer_start(m, st, 2.0 * M * (double)N * K);
+  if (r != hipSuccess) return r;
+  r = launch_gemm_fp8(A, lda, static_cast<const uint8_t*>(Bt), ldb, M, N, K, row_scale, w_scale, e, st);
+  if (r != hipSuccess) return r;
+  return timer_stop(m, st);
+}
+
 Epilogue epi(const float* bias, void* c0, int ld0, int split, void* c1 = nullptr, int ld1 = 0,
              int gelu = 0, int residual = 0, RowMap rows = RowMap::identity()) {
   Epilogue e;
@@ -330,10 +386,17 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
     }
     for (int l = 0; l < d.layers; ++l) {
       const LayerW& w = m->layers[l];
-      RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
-                              w.ln1_b, d.ln_eps, static_cast<T*>(m->h), st));
-      RUN(gemm(m, m->h, D, w.w_qkv_t, D, rows, 3 * D, D,
-               epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
+      if (m->fp8) {
+        RUN(launch_layernorm_fp8(static_cast<const bf16*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
+                                 w.ln1_b, d.ln_eps, m->h8, m->hs, st));
+        RUN(gemm8(m, m->h8, D, w.w_qkv_t, D, rows, 3 * D, D, m->hs, w.ws_qkv,
+                  epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
+      } else {
+        RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
+                                w.ln1_b, d.ln_eps, static_cast<T*>(m->h), st));
+        RUN(gemm(m, m->h, D, w.w_qkv_t, D, rows, 3 * D, D,
+                 epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
+      }
       AttnArgs a{};
       a.q = m->q; a.ldq = D;
       for (int tau = 0; tau <= t; ++tau) a.kv[tau] = kv_slot(m, l, tau, H);
@@ -342,9 +405,16 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
       a.scale = 1.0f / std::sqrt((float)a.dh);
       RUN(m->bf16 ? launch_attention_bf16(a, st) : launch_attention_f32(a, st));
       RUN(gemm(m, m->h, D, w.w_o_t, D, rows, D, D, epi(w.b_o, m->x, D, D, nullptr, 0, 0, 1), st));
-      RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
-                              w.ln2_b, d.ln_eps, static_cast<T*>(m->h), st));
-      RUN(gemm(m, m->h, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
+      if (m->fp8) {
+        RUN(launch_layernorm_fp8(static_cast<const bf16*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
+                                 w.ln2_b, d.ln_eps, m->h8, m->hs, st));
+        RUN(gemm8(m, m->h8, D, w.w_1_t, D, rows, F, D, m->hs, w.ws_1,
+                  epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
+      } else {
+        RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
+                                w.ln2_b, d.ln_eps, static_cast<T*>(m->h), st));
+        RUN(gemm(m, m->h, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
+      }
       RUN(gemm(m, m->u, F, w.w_2_t, F, rows, D, F, epi(w.b_2, m->x, D, D, nullptr, 0, 0, 1), st));
     }
     // final LayerNorm of the patch rows, then the out-projection to the encoder width

@@ -31,6 +31,9 @@ struct DeviceGuard {
 struct LayerW {
   float *ln1_g, *ln1_b, *b_qkv, *b_o, *ln2_g, *ln2_b, *b_1, *b_2;
   void *w_qkv_t, *w_o_t, *w_1_t, *w_2_t;   // transposed: [out, in]
+  // fp8 models: w_qkv_t and w_1_t hold e4m3 codes scaled by 1 / ws_*, and b_qkv,
+  // b_1 hold the biases divided by ws_* (what the fp8 GEMM epilogue expects)
+  float ws_qkv = 1.f, ws_1 = 1.f;
 };
 
 // Per-plan-shape device state: inputs copied in, per-round history out.
@@ -58,7 +61,8 @@ using GraphKey = std::tuple<int, int, int, int, uint32_t, uint32_t, int>;
 struct cem_model {
   cem_model_desc desc{};
   int device = 0;
-  bool bf16 = false;
+  bool bf16 = false;     // bf16 activations and weights (also for fp8 models)
+  bool fp8 = false;      // LayerNorm-fed projections with e4m3 operands
   size_t esz = 4;        // bytes per weight / activation element
   int B = 0;             // tokens per frame block
   long long rows_max = 0;
@@ -77,6 +81,8 @@ struct cem_model {
   // workspace
   void *x = nullptr, *h = nullptr, *q = nullptr, *u = nullptr, *kv = nullptr, *zhat = nullptr,
        *f0 = nullptr, *zobs_t = nullptr;
+  uint8_t* h8 = nullptr;   // fp8 models: e4m3 LayerNorm output [rows, d]
+  float* hs = nullptr;     // and its row scales [rows]
 
   cem::PlanState plan;
   hipStream_t cap_stream = nullptr;

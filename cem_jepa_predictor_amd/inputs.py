@@ -41,7 +41,7 @@ class ModelConfig:
     d_mlp: int
     patches: int          # P, patch tokens per frame block
     enc_dim: int          # E, encoder embedding width (projected in and out)
-    dtype: str            # "f32" or "bf16"
+    dtype: str            # "f32", "bf16", or "fp8" (bf16 with e4m3 LayerNorm-fed projections)
     max_horizon: int
     action_dim: int = ACTION_DIM
     state_dim: int = STATE_DIM
@@ -99,8 +99,14 @@ WORKLOADS: Dict[str, Workload] = {
     # output tiles in every projection.
     "oddk": Workload("oddk", ModelConfig("oddk", 2, 128, 2, 320, 16, 64, "bf16", 2),
                      PlanConfig(16, 4, 2, 2)),
+    # The small case with the fp8 (e4m3) q|k|v and MLP-up projections.
+    "small_fp8": Workload("small_fp8", ModelConfig("small_fp8", 6, 512, 8, 2048, 64, 512, "fp8", 3),
+                          PlanConfig(256, 32, 5, 3)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
+    # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.
+    "vjepa2ac_fp8": Workload("vjepa2ac_fp8", dataclasses.replace(_vj("vjepa2ac_fp8", 1, 1), dtype="fp8"),
+                             PlanConfig(800, 80, 10, 1)),
     # Same predictor, horizon 4 with a KV cache across frame blocks.
     "vjepa2ac_h4": Workload("vjepa2ac_h4", _vj("vjepa2ac_h4", 4, 4), PlanConfig(800, 80, 10, 4)),
 }
@@ -159,7 +165,7 @@ def make_weights(m: ModelConfig, seed: int = 0) -> Dict[str, np.ndarray]:
         if name.endswith("_g"):
             v = v + np.float32(1.0)
         v = v.astype(np.float32)
-        if m.dtype == "bf16":
+        if m.dtype in ("bf16", "fp8"):
             v = round_to_bf16(v)
         out[name] = v
     return out

@@ -51,7 +51,15 @@ typedef enum {
   CEM_E_INTERNAL = -6
 } cem_status;
 
-typedef enum { CEM_F32 = 0, CEM_BF16 = 1 } cem_dtype;
+/* Model / tensor element types.  CEM_FP8 (model dtype only): a bf16 model whose
+ * two LayerNorm-fed projections (fused q|k|v and MLP up) run on OCP fp8 e4m3
+ * operands (page section 06, "D. Model compression"; the 8-bit format of the
+ * gfx950 matrix cores): their weights quantized with one scale per matrix at
+ * create time, the LayerNorm outputs quantized per token row, fp32
+ * accumulation, both scales applied to the result; activations, every other
+ * projection, attention and the rollout output stay bf16.  Needs d_model % 512
+ * == 0. */
+typedef enum { CEM_F32 = 0, CEM_BF16 = 1, CEM_FP8 = 2 } cem_dtype;
 
 /* Predictor shape.  Frame block = 1 action token + 1 state token + `patches`
  * frame tokens (B = patches + 2).  d_model % heads == 0, head dim <= 128;
@@ -199,6 +207,14 @@ cem_status cem_warm_start(const float* mu_prev, const float* sigma_prev, int32_t
 cem_status cem_sample(const float* mu, const float* sigma, int32_t n, int32_t h, int32_t a,
                       uint64_t seed, uint32_t round, uint32_t plan_id, float lo, float hi,
                       float* actions, uint32_t* raw_words, void* stream);
+
+/* fp8 row quantization alone (the step that feeds CEM_FP8 projections): for each
+ * row r of x (device fp32 [rows, cols], cols % 8 == 0), scale[r] = amax_r / 448
+ * (1 for an all-zero row) and codes[r, c] = e4m3(clamp(x[r, c] * (448 / amax_r),
+ * -448, 448)), rounded to nearest even; codes device uint8 [rows, cols], scale
+ * device fp32 [rows]. */
+cem_status cem_fp8_quantize_rows(const float* x, int32_t rows, int32_t cols, uint8_t* codes,
+                                 float* scale, void* stream);
 
 /* Top-K alone: idx[k] = the k smallest (energy, index) pairs, ascending. */
 cem_status topk_select(const float* energy, int32_t n, int32_t k, int32_t* idx, void* stream);

@@ -42,7 +42,8 @@ def oracle_predictor(name: str):
     from oracle.predictor import Predictor
 
     wl, w, _, _, _, _ = workload_data(name)
-    return Predictor(w, wl.model.layers, wl.model.heads, wl.model.ln_eps)
+    return Predictor(w, wl.model.layers, wl.model.heads, wl.model.ln_eps,
+                     fp8_projections=wl.model.dtype == "fp8")
 
 
 _models = {}

@@ -45,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_weights_count_matches_canonical_layout(lib):
-    for name in ["tiny", "small", "vjepa2ac", "vjepa2ac_h4"]:
+    for name in ["tiny", "small", "vjepa2ac", "vjepa2ac_h4", "small_fp8"]:
         m = inputs.WORKLOADS[name].model
         desc = _lib.model_desc(m, 8)
         assert _lib.weights_count(desc) == inputs.weight_count(m)
@@ -167,3 +167,17 @@ def test_plan_batched_validates_null_model(lib):
     fake = ctypes.c_void_p(0x1000)
     assert lib.cem_plan_batched(None, ctypes.byref(p), 2, fake, fake, fake, fake, fake, fake, None,
                                 None) == -1
+
+
+
+def test_fp8_models_need_d_model_multiple_of_512(lib):
+    n = ctypes.c_size_t(0)
+    desc = _lib.model_desc(inputs.WORKLOADS["small_fp8"].model, 8)
+    assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == 0
+    desc = _lib.model_desc(inputs.WORKLOADS["oddk"].model, 8)
+    desc.dtype = 2
+    assert lib.cem_weights_count(ctypes.byref(desc), ctypes.byref(n)) == -2
+    assert "512" in lib.cem_last_error().decode()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.cem_fp8_quantize_rows(fake, 4, 12, fake, fake, None) == -2
+    assert lib.cem_fp8_quantize_rows(None, 4, 16, fake, fake, None) == -1

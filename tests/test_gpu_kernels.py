@@ -204,3 +204,25 @@ def test_warm_start_bit_exact(gpu_lib, h, a, floor):
     for got_mu, got_sigma in ((mo, so), (mt, st)):
         np.testing.assert_array_equal(to_np(got_mu), want_mu)
         np.testing.assert_array_equal(to_np(got_sigma), want_sigma)
+
+
+@pytest.mark.parametrize("rows,cols", [(37, 1024), (5, 8), (64, 512)])
+def test_fp8_quantize_rows_bit_exact(gpu_lib, rows, cols):
+    """The device's e4m3 row quantization (scale and every code) equals the oracle's."""
+    import torch
+    from cem_jepa_predictor_amd import _lib
+    from oracle import fp8
+
+    log(f"fp8 quantize rows={rows} cols={cols}")
+    rng = np.random.default_rng(rows * cols)
+    x = (rng.standard_normal((rows, cols)) * rng.choice([1e-3, 1.0, 50.0], (rows, 1))).astype(np.float32)
+    x[0] = 0.0
+    if rows > 3:
+        x[3, :4] = [448.0, -1e-9, 2.0 ** -12, 3.0]
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
+    scale = torch.empty(rows, dtype=torch.float32, device="cuda")
+    _lib.fp8_quantize_rows(to_dev(x), codes, scale)
+    torch.cuda.synchronize()
+    want_codes, want_scale = fp8.quantize_rows(x)
+    np.testing.assert_array_equal(to_np(scale), want_scale)
+    np.testing.assert_array_equal(to_np(codes), want_codes)

@@ -23,7 +23,7 @@ from .gpu_util import (gpu_model, log, max_rel, oracle_predictor, release_models
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-5, "bf16": 2e-2}
+TOL = {"f32": 1e-5, "bf16": 2e-2, "fp8": 2e-2}
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -38,14 +38,14 @@ def gpu_rollout(name, actions):
     wl, _, _, z_obs, _, s0 = workload_data(name)
     m = wl.model
     model = gpu_model(name)
-    dt = torch.bfloat16 if m.dtype == "bf16" else torch.float32
+    dt = torch.float32 if m.dtype == "f32" else torch.bfloat16
     zp = torch.empty((actions.shape[0], m.patches, m.enc_dim), dtype=dt, device="cuda")
     model.rollout(to_dev(actions), to_dev(z_obs), to_dev(s0), zp)
     torch.cuda.synchronize()
     return to_np(zp)
 
 
-@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("oddk", 9)])
+@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("oddk", 9), ("small_fp8", 12)])
 def test_rollout_matches_oracle(gpu_lib, name, n):
     from cem_jepa_predictor_amd import inputs
 
@@ -61,7 +61,11 @@ def test_rollout_matches_oracle(gpu_lib, name, n):
     scale = np.abs(want).max()
     log(f"  energy max rel err {rel:.3e}; z max abs err {np.abs(got - want).max():.3e} (scale {scale:.2f})")
     assert rel <= TOL[wl.model.dtype]
-    ztol = 1e-4 if wl.model.dtype == "f32" else 5e-2
+    # element-wise bound on the predicted frame: fp8 models flip an e4m3 rounding of the
+    # LayerNorm outputs wherever GPU (bf16 residual stream) and oracle (float64) land on
+    # either side of a step, which moves single elements by up to ~7 % of the frame's
+    # largest magnitude after six layers; energies average it out
+    ztol = {"f32": 1e-4, "bf16": 5e-2, "fp8": 1.5e-1}[wl.model.dtype]
     assert np.abs(got - want).max() <= ztol * scale
     if n >= 8:
         # energy parity as a ranking: Pearson r of GPU vs oracle energies across the
@@ -324,3 +328,20 @@ def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
         np.testing.assert_array_equal(tb["sg"][:, b], t1["sg"][:, 0])
     # the problems really differ
     assert not np.array_equal(tb["e"][:, :N], tb["e"][:, N:2 * N])
+
+
+def test_plan_small_fp8_lockstep_sampled(gpu_lib):
+    """fp8 q|k|v and MLP-up projections (model dtype CEM_FP8) against the oracle's
+    fp8-projection predictor, round by round."""
+    log("plan small_fp8 lockstep, 6 oracle candidates per round")
+    out = run_plan("small_fp8")
+    worst = _lockstep("small_fp8", out, lambda r, n: np.random.default_rng(r).choice(n, 6, replace=False))
+    log(f"  worst energy rel err {worst:.3e}")
+
+
+def test_plan_vjepa2ac_fp8_full_size_lockstep(gpu_lib):
+    """The V-JEPA2-AC shape with fp8 projections, 800 candidates x 2 rounds."""
+    log("plan vjepa2ac_fp8 (N=800, R=2) lockstep, oracle on 2 candidates")
+    out = run_plan("vjepa2ac_fp8", rounds=2)
+    worst = _lockstep("vjepa2ac_fp8", out, lambda r, n: np.array([5 + 300 * r, 777 - r]))
+    log(f"  worst energy rel err {worst:.3e}")
