@@ -55,8 +55,14 @@
 //    fit the register budget of two waves per SIMD).  Row scales of A and one
 //    scale for all of B are applied in the epilogue; the bias enters the
 //    accumulators divided by both.  Plain and GELU epilogues.
+//  * Affine rows (bf16): a LayerNorm folded into the projection after it, so
+//    A is the raw residual stream and a per-row scale / shift and per-column
+//    term are applied around the contraction (see the kernel's comment).
+//  * Tile start: one MFMA per 32 x 32 block writes the bias (and the affine
+//    row terms) into the accumulators from per-lane factors that were loaded
+//    with bounds-checked buffer loads during the previous tile's first slab.
 //
-// Epilogue (fp32): + bias (preloaded into the accumulators), optional GELU,
+// Epilogue (fp32): + bias (already in the accumulators), optional GELU,
 // optional residual add (the output already holds the residual stream),
 // optional column split into two destinations (q -> Q buffer, k|v -> KV
 // cache), optional output-row remap.
@@ -64,6 +70,18 @@
 
 namespace cem {
 namespace {
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// LDS store that the compiler does not order against the operand loads in flight
+// (it would wait for every outstanding buffer_load ... lds before any LDS store it
+// cannot prove disjoint from them).  Used where the target region is known to be
+// out of reach of every load in flight; the asm's memory clobber keeps later LDS
+// reads behind it, and one wave's LDS accesses complete in order.
+__device__ __forceinline__ void lds_write_b64(uint8_t* p, uint2 v) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+  asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
 
 // ------------------------------------------------------------------ epilogue
 template <typename T> struct Store4;
@@ -126,7 +144,6 @@ constexpr int NE = 5;                       // entries in the operand ring
 constexpr int ENT = BM * BK * 2;            // 32 KB: one operand slab (256 rows x 128 B)
 constexpr int GROUP_M = 8;
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 struct TileCoord {
   int m0, n0, rows_a, rows_b;   // rows_a = rows_b = 0: no tile (loads read zeros)
@@ -146,16 +163,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, in
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
-// F8: operands are OCP fp8 e4m3 codes; A row m is scaled by row_scale[m] and all of
-// Bt by w_scale, so out = row_scale[m] w_scale (A Bt^T)[m, n] + bias[n].  The bias
-// enters the accumulators divided by both scales (epi.bias holds bias / w_scale).
-template <int KIND, bool F8>
+// AFF (affine rows): out = s_m ((A Bt^T)[m, n] - shift_m col_n) + w_scale bias_n with
+// s_m = scale_m w_scale.  row_vals holds scale[M] and, when nrow == 2, shift[M] right
+// after it; epi.bias holds bias[N] and, when ncol == 2, col[N] right after it (missing
+// parts read as zero).  The accumulators start at bias_n / scale_m - shift_m col_n and
+// the epilogue multiplies by s_m.
+//  * F8 (implies AFF): operands are OCP fp8 e4m3 codes, A row m scaled by scale_m
+//    and all of Bt by w_scale; epi.bias holds bias / w_scale.
+//  * bf16 with AFF: a LayerNorm folded into the projection that follows it,
+//    LN(x) W = rstd (x W' - mean 1^T W') + beta W with W' = diag(gamma) W:
+//    scale = rstd, shift = mean, col = 1^T W', bias = b + beta W.
+template <int KIND, bool F8, bool AFF>
 __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict__ A, int lda,
                                                          const void* __restrict__ Bt, int ldb,
                                                          int M, int N, int K, Epilogue epi,
-                                                         const float* __restrict__ row_scale,
-                                                         float w_scale) {
-  static_assert(!(F8 && KIND == kEpiResidual), "fp8 operands feed the plain and GELU epilogues only");
+                                                         const float* __restrict__ row_vals,
+                                                         int nrow, float w_scale, int ncol) {
+  static_assert(AFF || !F8, "fp8 operands always carry row scales");
+  static_assert(!(AFF && KIND == kEpiResidual), "row scaling feeds the plain and GELU epilogues only");
   constexpr int ES = F8 ? 1 : 2;             // operand bytes per element
   constexpr int KS = F8 ? BK8 : BK;          // k-values per slab
   __shared__ __attribute__((aligned(1024))) uint8_t lds[NE * ENT];
@@ -243,7 +268,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
   auto mfma8 = [&](int buf, int i, int j) {
     acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(gb[buf][j], ga[i], acc[i][j], 0, 0, 0, 0, 0, 0);
   };
-  float rsc[4] = {1.f, 1.f, 1.f, 1.f};   // fp8: row_scale of the lane's row in each 32-row block
+  float rsc[4] = {1.f, 1.f, 1.f, 1.f};   // AFF: s_m of the lane's row in each 32-row block
   auto frag1 = [&](int ea, int s, int buf, int r) {
     const int pc = ((2 * s + fk) ^ fsw) << 4;
     if (r < 4) {
@@ -259,33 +284,84 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
     const int i = idx >> 1, j = idx & 1;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[buf][j], fa[buf][i], acc[i][j], 0, 0, 0);
   };
-  // accumulators start at the bias (lane quads are 4 consecutive output columns);
-  // fp8: at bias / (row_scale w_scale), and the lane's row scales are kept
-  auto init_acc = [&](const TileCoord& t) {
-    const int cb = t.n0 + wn * 64 + 4 * fk;
-    float inv[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (F8) {
+  // The accumulators start at A0[m, n] = bias_n / scale_m - shift_m col_n (bias_n
+  // without AFF): a sum of two rank-1 terms, so one MFMA per 32 x 32 block writes it.
+  // Lanes 0..31 bring the scale of row fr of each 32-row block and the bias of column
+  // fr of each 32-column block, lanes 32..63 the shift and col.  Each fp32 factor is
+  // split into three bf16 parts (v = v1 + v2 + v3, exact); k-slots 0..5 (lanes 0..31)
+  // carry the six largest cross terms of (1 / scale)(bias), slots 8..13 (lanes 32..63)
+  // those of (-shift)(col), leaving a relative error near 2^-24 per term.
+  //
+  // The factors come through bounds-checked buffer loads (out of range reads zero, so
+  // a missing part costs nothing and needs no branch) into registers, issued for the
+  // next tile during the current tile's first slab, just before its B loads: they land
+  // as early as those instead of stalling the restart at the tile boundary.
+  const __amdgpu_buffer_rsrc_t rrow = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(row_vals), (short)0, AFF && row_vals ? nrow * M * 4 : 0, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rcol = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(epi.bias), (short)0, epi.bias ? (AFF ? ncol : 1) * N * 4 : 0, 0x00020000);
+  float nrv[4] = {1.f, 1.f, 1.f, 1.f}, ncv[2] = {0.f, 0.f};
+  auto load_consts = [&](const TileCoord& t) {
+    // lanes 32..63 read part 2 (shift, col); an exhausted grid reads out of range
+    const int rbase = t.rows_a ? t.m0 + wm * 128 + fr + fk * M : 0x7fffffff / 4 - 256;
+    const int cbase = t.rows_b ? t.n0 + wn * 64 + fr + fk * N : 0x7fffffff / 4 - 64;
+    if constexpr (AFF) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int m = t.m0 + wm * 128 + 32 * i + fr;
-        rsc[i] = (m < M) ? row_scale[m] : 1.f;
-        inv[i] = __builtin_amdgcn_rcpf(rsc[i]);
-        rsc[i] *= w_scale;
+        // rows past M read out of range (zero), also from part 2
+        const int off = m < M ? (rbase + 32 * i) * 4 : 0x7ffffff0;
+        nrv[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rrow, off, 0, 0));
       }
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) {
+      const int n = t.n0 + wn * 64 + 32 * j + fr;
+      const int off = n < N ? (cbase + 32 * j) * 4 : 0x7ffffff0;
+      ncv[j] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rcol, off, 0, 0));
+    }
+  };
+  auto init_acc = [&]() {
+    float sv[4], tv[2];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = cb + j * 32 + 8 * q;
-        float4 bb = make_float4(0.f, 0.f, 0.f, 0.f);
-        if (epi.bias && c < N) bb = *reinterpret_cast<const float4*>(epi.bias + c);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          acc[i][j][4 * q] = bb.x * inv[i]; acc[i][j][4 * q + 1] = bb.y * inv[i];
-          acc[i][j][4 * q + 2] = bb.z * inv[i]; acc[i][j][4 * q + 3] = bb.w * inv[i];
-        }
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = fk == 0 ? 1.f : 0.f;
+      if constexpr (AFF) {
+        // rows past M read scale 0: their results are never stored
+        sv[i] = fk == 0 ? __builtin_amdgcn_rcpf(nrv[i]) : -nrv[i];
+        // every lane scales its rows in the epilogue: lanes 32..63 take lane - 32's
+        rsc[i] = __shfl(nrv[i], fr, 64) * w_scale;
       }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) tv[j] = ncv[j];
+    auto split3 = [](float v, uint32_t& h1, uint32_t& h2, uint32_t& h3) {
+      h1 = f32_to_bf16(v);
+      const float r1 = v - __uint_as_float(h1 << 16);
+      h2 = f32_to_bf16(r1);
+      h3 = f32_to_bf16(r1 - __uint_as_float(h2 << 16));
+    };
+    bf16x8_t U[4], V[2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t h1, h2, h3;
+      split3(sv[i], h1, h2, h3);
+      // slots: s1 s1 s2 s1 s2 s3 0 0
+      U[i] = __builtin_bit_cast(bf16x8_t, u32x4{h1 | (h1 << 16), h2 | (h1 << 16), h2 | (h3 << 16), 0u});
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      uint32_t h1, h2, h3;
+      split3(tv[j], h1, h2, h3);
+      // slots: t1 t2 t1 t3 t2 t1 0 0
+      V[j] = __builtin_bit_cast(bf16x8_t, u32x4{h1 | (h2 << 16), h1 | (h3 << 16), h2 | (h1 << 16), 0u});
+    }
+    const f32x16_t zero = {};
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(V[j], U[i], zero, 0, 0, 0);
   };
 #define CEM_WAIT(vm) __builtin_amdgcn_s_waitcnt(((vm) & 15) | (((vm) >> 4) << 14) | (0 << 8) | 0x0070)
 #define F __builtin_amdgcn_sched_barrier(0)
@@ -294,7 +370,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
   TileCoord T = coord(0), T1 = coord(1), T2 = coord(2);
   if (T.rows_a == 0) return;   // no tile for this workgroup (uniform)
   auto tile_at = [&](int off) -> TileCoord { return off == 0 ? T : (off == 1 ? T1 : T2); };
-  init_acc(T);
+  load_consts(T);
+  init_acc();
   F;
   // prologue: A and B of slabs 0 and 1 into entries 0..3
   {
@@ -357,6 +434,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
       // fp8 substep 1: slab s + 1's first fragments; B of slab s + 2
       mfma8(1, 0, 0); F; frag8b(ea_n, 0, 0, 0); F;
       mfma8(1, 0, 1); F; frag8b(ea_n, 0, 0, 1); F; frag8a(ea_n, 0, 0); F;
+      if (kt == 0) load_consts(T1);
+      F;
       mfma8(1, 1, 0); F; dma_b(Tt, tkt, ea, 0); F;
       mfma8(1, 1, 1); F; frag8a(ea_n, 0, 1); F; dma_b(Tt, tkt, ea, 1); F;
       mfma8(1, 2, 0); F; dma_b(Tt, tkt, ea, 2); F;
@@ -395,6 +474,8 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
       mfma1(1, 0); F; frag1(ea_n, 0, 0, 0); F; frag1(ea_n, 0, 0, 1); F;
       mfma1(1, 1); F; frag1(ea_n, 0, 0, 2); F; frag1(ea_n, 0, 0, 3); F;
       mfma1(1, 2); F; frag1(ea_n, 0, 0, 4); F; frag1(ea_n, 0, 0, 5); F;
+      if (kt == 0) load_consts(T1);
+      F;
       mfma1(1, 3); F;
       dma_b(Tt, tkt, ea, 0); F;
       mfma1(1, 4); F;
@@ -501,7 +582,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
             for (int q = 0; q < 4; ++q) {
               float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                             acc[i][j][4 * q + 3]};
-              if constexpr (F8) {
+              if constexpr (AFF) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) v[e] *= rsc[i];
               }
@@ -513,7 +594,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
               u.x = pack_bf16x2(v[0], v[1]);
               u.y = pack_bf16x2(v[2], v[3]);
               const int c16 = 4 * j + q;
-              *reinterpret_cast<uint2*>(ep + fr * 128 + ((c16 ^ ((fr >> 1) & 7)) << 4) + fk * 8) = u;
+              lds_write_b64(ep + fr * 128 + ((c16 ^ ((fr >> 1) & 7)) << 4) + fk * 8, u);
             }
           u32x4 d[4];
 #pragma unroll
@@ -544,7 +625,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
           for (int q = 0; q < 4; ++q) {
             float v[4] = {acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
                           acc[i][j][4 * q + 3]};
-            if constexpr (F8) {
+            if constexpr (AFF) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] *= rsc[i];
             }
@@ -561,7 +642,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
     T1 = T2;
     T2 = coord(ti + 3);
     --toff;
-    init_acc(T);
+    init_acc();
     F;
   }
   CEM_WAIT(0);   // drain the dummy loads of the slabs past the last tile
@@ -651,14 +732,30 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
   const int grid = tiles < cus ? tiles : cus;   // persistent: one workgroup per CU
   switch (epi_kind(epi)) {
     case kEpiGelu:
-      gemm_bf16_kernel<kEpiGelu, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 1.f);
+      gemm_bf16_kernel<kEpiGelu, false, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 0, 1.f, 1);
       break;
     case kEpiResidual:
-      gemm_bf16_kernel<kEpiResidual, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 1.f);
+      gemm_bf16_kernel<kEpiResidual, false, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 0, 1.f, 1);
       break;
     default:
-      gemm_bf16_kernel<kEpiPlain, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 1.f);
+      gemm_bf16_kernel<kEpiPlain, false, false><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, nullptr, 0, 1.f, 1);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_bf16_rows(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N, int K,
+                                 const float* row_vals, const Epilogue& epi, hipStream_t stream) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (K <= 0 || K % BK != 0 || !row_vals || epi.residual) return hipErrorInvalidValue;
+  int cus = 0;
+  const hipError_t ce = cu_count(&cus);
+  if (ce != hipSuccess) return ce;
+  const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int grid = tiles < cus ? tiles : cus;
+  if (epi.gelu)
+    gemm_bf16_kernel<kEpiGelu, false, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_vals, 2, 1.f, 2);
+  else
+    gemm_bf16_kernel<kEpiPlain, false, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_vals, 2, 1.f, 2);
   return hipGetLastError();
 }
 
@@ -673,9 +770,9 @@ hipError_t launch_gemm_fp8(const uint8_t* A, int lda, const uint8_t* Bt, int ldb
   const int tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int grid = tiles < cus ? tiles : cus;
   if (epi.gelu)
-    gemm_bf16_kernel<kEpiGelu, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_scale, w_scale);
+    gemm_bf16_kernel<kEpiGelu, true, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_scale, 1, w_scale, 1);
   else
-    gemm_bf16_kernel<kEpiPlain, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_scale, w_scale);
+    gemm_bf16_kernel<kEpiPlain, true, true><<<grid, NTHR, 0, stream>>>(A, lda, Bt, ldb, M, N, K, epi, row_scale, 1, w_scale, 1);
   return hipGetLastError();
 }
 

@@ -47,6 +47,10 @@ bool layernorm_supports(int d);
 hipError_t launch_layernorm_fp8(const bf16* x, int rows, int d, RowMap in_rows, const float* g,
                                 const float* b, float eps, uint8_t* y8, float* row_scale,
                                 hipStream_t stream);
+// Row statistics of bf16 rows [rows, d] (d % 128 == 0): mean[r] and rstd[r] =
+// 1 / sqrt(biased variance + eps), fp32, the LayerNorm kernel's arithmetic.
+hipError_t launch_row_stats(const bf16* x, int rows, int d, float eps, float* mean, float* rstd,
+                            hipStream_t stream);
 // The same per-row quantization of fp32 rows [rows, cols] (cols % 8 == 0).
 hipError_t launch_quantize_rows_fp8(const float* x, int rows, int cols, uint8_t* y8,
                                     float* row_scale, hipStream_t stream);
@@ -58,6 +62,13 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
                             int K, const Epilogue& epi, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N,
                            int K, const Epilogue& epi, hipStream_t stream);
+// bf16 with affine rows (a LayerNorm folded into the projection that follows it):
+// out = epilogue(scale[m] ((A Bt^T)[m, n] - shift[m] col[n]) + bias[n]) with
+// row_vals = [scale[M] | shift[M]] and epi.bias = [bias[N] | col[N]] (one array
+// each, the second part right after the first); plain or GELU epilogue; K % 64 == 0.
+hipError_t launch_gemm_bf16_rows(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N,
+                                 int K, const float* row_vals, const Epilogue& epi,
+                                 hipStream_t stream);
 // fp8 operands (OCP e4m3 codes): out = epilogue(row_scale[m] * w_scale * (A Bt^T)[m, n]
 // + bias[n]) with epi.bias holding bias / w_scale; plain or GELU epilogue only;
 // K % 128 == 0 (hipErrorInvalidValue otherwise).

@@ -213,6 +213,57 @@ __global__ __launch_bounds__(256) void quantize_rows_fp8_kernel(const float* __r
   if (lane == 0) row_scale[r] = scale;
 }
 
+// Row statistics only (a LayerNorm folded into the GEMM that consumes its rows):
+// mean and rstd of bf16 rows with the arithmetic of the kernels above.  VEC = 8:
+// d = 512 * N, 16-byte runs; VEC = 2: d = 128 * N, bf16 pairs.  Reads d elements
+// and writes 8 bytes per row.
+template <int VEC, int N>
+__global__ __launch_bounds__(256) void row_stats_kernel(const bf16* __restrict__ x, int rows,
+                                                        float eps, float* __restrict__ mean_out,
+                                                        float* __restrict__ rstd_out) {
+  constexpr int d = 64 * VEC * N;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float v[VEC * N];
+  float s = 0.f;
+  if constexpr (VEC == 8) {
+    const uint4* src = reinterpret_cast<const uint4*>(x + (long long)r * d);
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const uint4 u = src[c * 64 + lane];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * c + 2 * k] = __uint_as_float(w[k] << 16);
+        v[8 * c + 2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+        s += v[8 * c + 2 * k] + v[8 * c + 2 * k + 1];
+      }
+    }
+  } else {
+    const uint32_t* src = reinterpret_cast<const uint32_t*>(x + (long long)r * d);
+#pragma unroll
+    for (int c = 0; c < N; ++c) {
+      const uint32_t u = src[c * 64 + lane];
+      v[2 * c] = __uint_as_float(u << 16);
+      v[2 * c + 1] = __uint_as_float(u & 0xffff0000u);
+      s += v[2 * c] + v[2 * c + 1];
+    }
+  }
+  const float mean = wave_sum(s) * (1.0f / d);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < VEC * N; ++i) {
+    const float t = v[i] - mean;
+    q += t * t;
+  }
+  const float rstd = rsqrtf(wave_sum(q) * (1.0f / d) + eps);
+  if (lane == 0) {
+    mean_out[r] = mean;
+    rstd_out[r] = rstd;
+  }
+}
+
 template <int NCH, typename T>
 hipError_t run(const T* x, int rows, RowMap in_rows, const float* g, const float* b, float eps,
                T* y, hipStream_t stream) {
@@ -277,6 +328,27 @@ hipError_t launch_layernorm_fp8(const bf16* x, int rows, int d, RowMap in_rows, 
     case 4096: layernorm_fp8_kernel<8><<<grid, 256, 0, stream>>>(x, rows, in_rows, g, b, eps, y8, row_scale); break;
     default: return hipErrorInvalidValue;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats(const bf16* x, int rows, int d, float eps, float* mean, float* rstd,
+                            hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  const int grid = (rows + 3) / 4;
+#define CEM_STATS(V, N) row_stats_kernel<V, N><<<grid, 256, 0, stream>>>(x, rows, eps, mean, rstd); break
+  switch (d) {
+    case 128: CEM_STATS(2, 1);
+    case 256: CEM_STATS(2, 2);
+    case 384: CEM_STATS(2, 3);
+    case 512: CEM_STATS(8, 1);
+    case 768: CEM_STATS(2, 6);
+    case 1024: CEM_STATS(8, 2);
+    case 1536: CEM_STATS(8, 3);
+    case 2048: CEM_STATS(8, 4);
+    case 4096: CEM_STATS(8, 8);
+    default: return hipErrorInvalidValue;
+  }
+#undef CEM_STATS
   return hipGetLastError();
 }
 

@@ -137,6 +137,7 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   m->device = device;
   m->bf16 = d.dtype != CEM_F32;
   m->fp8 = d.dtype == CEM_FP8;
+  m->ln_fold = d.dtype == CEM_BF16;
   m->esz = m->bf16 ? 2 : 4;
   m->B = d.patches + 2;
   m->rows_max = (long long)d.max_samples * m->B;
@@ -149,15 +150,18 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   const size_t o_w_in = wl.take(D * E * es), o_b_in = wl.take(D * 4);
   const size_t o_w_a = wl.take(A * D * 4), o_b_a = wl.take(D * 4);
   const size_t o_w_s = wl.take(S * D * 4), o_b_s = wl.take(D * 4);
-  struct LO { size_t ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_1, b_1, w_2, b_2; };
+  struct LO {
+    size_t ln1_g, ln1_b, w_qkv, b_qkv, w_o, b_o, ln2_g, ln2_b, w_1, b_1, w_2, b_2;
+  };
   std::vector<LO> lo(L);
+  const size_t fold = m->ln_fold ? 1 : 0;
   for (size_t l = 0; l < L; ++l) {
     lo[l].ln1_g = wl.take(D * 4); lo[l].ln1_b = wl.take(D * 4);
     const size_t es8 = m->fp8 ? 1 : es;   // fp8 models: e4m3 codes for q|k|v and MLP up
-    lo[l].w_qkv = wl.take(3 * D * D * es8); lo[l].b_qkv = wl.take(3 * D * 4);
+    lo[l].w_qkv = wl.take(3 * D * D * es8); lo[l].b_qkv = wl.take((1 + fold) * 3 * D * 4);
     lo[l].w_o = wl.take(D * D * es); lo[l].b_o = wl.take(D * 4);
     lo[l].ln2_g = wl.take(D * 4); lo[l].ln2_b = wl.take(D * 4);
-    lo[l].w_1 = wl.take(F * D * es8); lo[l].b_1 = wl.take(F * 4);
+    lo[l].w_1 = wl.take(F * D * es8); lo[l].b_1 = wl.take((1 + fold) * F * 4);
     lo[l].w_2 = wl.take(D * F * es); lo[l].b_2 = wl.take(D * 4);
   }
   const size_t o_lnf_g = wl.take(D * 4), o_lnf_b = wl.take(D * 4);
@@ -205,6 +209,35 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
       }
     src += in * outd;
   };
+  // LayerNorm fold (x - mean) rstd gamma W + beta W + b = rstd (x W' - mean 1^T W') + b'
+  // with W' = diag(gamma) W: stores bf16(W') transposed, and at b_off b' = b + beta W
+  // (from the unrounded W) followed by the column sums of the bf16 W' values (so the
+  // mean term cancels exactly what the GEMM contracts).  gamma and beta are the `in`
+  // values just before the matrix in the flat buffer.
+  auto put_mat_t_folded = [&](size_t off, size_t in, size_t outd, size_t b_off) {
+    const size_t cs_off = b_off + outd * 4;
+    const float* g = src - 2 * in;
+    const float* beta = src - in;
+    const float* bias = src + in * outd;
+    std::vector<double> cs(outd, 0.0), bb(outd, 0.0);
+    for (size_t i = 0; i < in; ++i)
+      for (size_t o = 0; o < outd; ++o) {
+        const float v = src[i * outd + o];
+        const uint16_t b = host_bf16(g[i] * v);
+        std::memcpy(hw.data() + off + (o * in + i) * 2, &b, 2);
+        uint32_t u = (uint32_t)b << 16;
+        float f;
+        std::memcpy(&f, &u, 4);
+        cs[o] += (double)f;
+        bb[o] += (double)beta[i] * (double)v;
+      }
+    for (size_t o = 0; o < outd; ++o) {
+      const float c = (float)cs[o], bo = (float)((double)bias[o] + bb[o]);
+      std::memcpy(hw.data() + cs_off + o * 4, &c, 4);
+      std::memcpy(hw.data() + b_off + o * 4, &bo, 4);
+    }
+    src += in * outd + outd;   // the matrix and its bias
+  };
   auto put_vec_scaled = [&](size_t off, size_t count, float ws) {
     for (size_t i = 0; i < count; ++i) {
       const float v = src[i] / ws;
@@ -218,10 +251,12 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   for (size_t l = 0; l < L; ++l) {
     put_vec(lo[l].ln1_g, D); put_vec(lo[l].ln1_b, D);
     if (m->fp8) { put_mat_t8(lo[l].w_qkv, D, 3 * D, ws_qkv[l]); put_vec_scaled(lo[l].b_qkv, 3 * D, ws_qkv[l]); }
+    else if (m->ln_fold) put_mat_t_folded(lo[l].w_qkv, D, 3 * D, lo[l].b_qkv);
     else { put_mat_t(lo[l].w_qkv, D, 3 * D); put_vec(lo[l].b_qkv, 3 * D); }
     put_mat_t(lo[l].w_o, D, D); put_vec(lo[l].b_o, D);
     put_vec(lo[l].ln2_g, D); put_vec(lo[l].ln2_b, D);
     if (m->fp8) { put_mat_t8(lo[l].w_1, D, F, ws_1[l]); put_vec_scaled(lo[l].b_1, F, ws_1[l]); }
+    else if (m->ln_fold) put_mat_t_folded(lo[l].w_1, D, F, lo[l].b_1);
     else { put_mat_t(lo[l].w_1, D, F); put_vec(lo[l].b_1, F); }
     put_mat_t(lo[l].w_2, F, D); put_vec(lo[l].b_2, D);
   }
@@ -261,12 +296,14 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   const size_t o_zhat = al.take((size_t)d.max_samples * P * E * es);
   const size_t o_f0 = al.take(P * D * es), o_zobs = al.take(P * E * es);
   const size_t o_h8 = al.take(m->fp8 ? rows * D : 0), o_hs = al.take(m->fp8 ? rows * 4 : 0);
+  const size_t o_stats = al.take(fold * 2 * rows * 4);
   e = hipMalloc(&m->arena, al.off);
   if (e != hipSuccess) return fail(hip_status(e, "hipMalloc(workspace)"));
   uint8_t* ab = static_cast<uint8_t*>(m->arena);
   m->x = ab + o_x; m->h = ab + o_h; m->q = ab + o_q; m->u = ab + o_u; m->kv = ab + o_kv;
   m->zhat = ab + o_zhat; m->f0 = ab + o_f0; m->zobs_t = ab + o_zobs;
   if (m->fp8) { m->h8 = ab + o_h8; m->hs = reinterpret_cast<float*>(ab + o_hs); }
+  if (m->ln_fold) m->ln_stats = reinterpret_cast<float*>(ab + o_stats);
 
   e = select_init();
   if (e != hipSuccess) return fail(hip_status(e, "select_init"));
@@ -336,6 +373,22 @@ hipError_t gemm8(cem_model* m, const uint8_t* A, int lda, const void* Bt, int ld
   return timer_stop(m, st);
 }
 
+// bf16 GEMM over M raw residual rows with the LayerNorm before it folded in: row
+// statistics of those rows, then the GEMM with rstd / mean row terms and the folded
+// bias / column-sum terms (e.bias, 2 N floats)
+hipError_t gemm_ln(cem_model* m, const void* A, int lda, const void* Bt, int ldb, int M, int N, int K,
+                   const Epilogue& e, hipStream_t st) {
+  hipError_t r = launch_row_stats(static_cast<const bf16*>(A), M, K, m->desc.ln_eps,
+                                  m->ln_stats + M, m->ln_stats, st);
+  if (r != hipSuccess) return r;
+  r = timer_start(m, st, 2.0 * M * (double)N * K);
+  if (r != hipSuccess) return r;
+  r = launch_gemm_bf16_rows(static_cast<const bf16*>(A), lda, static_cast<const bf16*>(Bt), ldb, M,
+                            N, K, m->ln_stats, e, st);
+  if (r != hipSuccess) return r;
+  return timer_stop(m, st);
+}
+
 Epilogue epi(const float* bias, void* c0, int ld0, int split, void* c1 = nullptr, int ld1 = 0,
              int gelu = 0, int residual = 0, RowMap rows = RowMap::identity()) {
   Epilogue e;
@@ -391,6 +444,9 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
                                  w.ln1_b, d.ln_eps, m->h8, m->hs, st));
         RUN(gemm8(m, m->h8, D, w.w_qkv_t, D, rows, 3 * D, D, m->hs, w.ws_qkv,
                   epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
+      } else if (m->ln_fold) {
+        RUN(gemm_ln(m, m->x, D, w.w_qkv_t, D, rows, 3 * D, D,
+                    epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
       } else {
         RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
                                 w.ln1_b, d.ln_eps, static_cast<T*>(m->h), st));
@@ -410,6 +466,8 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
                                  w.ln2_b, d.ln_eps, m->h8, m->hs, st));
         RUN(gemm8(m, m->h8, D, w.w_1_t, D, rows, F, D, m->hs, w.ws_1,
                   epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
+      } else if (m->ln_fold) {
+        RUN(gemm_ln(m, m->x, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
       } else {
         RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
                                 w.ln2_b, d.ln_eps, static_cast<T*>(m->h), st));

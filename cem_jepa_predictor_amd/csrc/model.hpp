@@ -34,6 +34,9 @@ struct LayerW {
   // fp8 models: w_qkv_t and w_1_t hold e4m3 codes scaled by 1 / ws_*, and b_qkv,
   // b_1 hold the biases divided by ws_* (what the fp8 GEMM epilogue expects)
   float ws_qkv = 1.f, ws_1 = 1.f;
+  // LayerNorm-folded bf16 models: w_qkv_t and w_1_t hold bf16(diag(gamma) W) for the
+  // LayerNorm before them, and b_qkv, b_1 hold [b + beta W | column sums of those bf16
+  // values] (2 x out floats)
 };
 
 // Per-plan-shape device state: inputs copied in, per-round history out.
@@ -63,6 +66,7 @@ struct cem_model {
   int device = 0;
   bool bf16 = false;     // bf16 activations and weights (also for fp8 models)
   bool fp8 = false;      // LayerNorm-fed projections with e4m3 operands
+  bool ln_fold = false;  // bf16: LN1 / LN2 folded into the q|k|v and MLP-up GEMMs
   size_t esz = 4;        // bytes per weight / activation element
   int B = 0;             // tokens per frame block
   long long rows_max = 0;
@@ -83,6 +87,7 @@ struct cem_model {
        *f0 = nullptr, *zobs_t = nullptr;
   uint8_t* h8 = nullptr;   // fp8 models: e4m3 LayerNorm output [rows, d]
   float* hs = nullptr;     // and its row scales [rows]
+  float* ln_stats = nullptr;   // LayerNorm-folded models: [rstd | mean] of the rows of one call
 
   cem::PlanState plan;
   hipStream_t cap_stream = nullptr;
