@@ -49,8 +49,8 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
 # as null once those change.
 GEMM_COUNTERS = {
-    "sources_sha256": "562efd2f9735cff597e89b1ce2b8b74964cde96b458d94903e1bb67d9c452ba3",
-    "bytes_per_launch": 3678077056,
+    "sources_sha256": "bd1c43f3eef799f9b21ca0b12475a3ea7a80baa68b4a6075c36f67222d7f2e15",
+    "bytes_per_launch": 3659552843,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 
