@@ -70,7 +70,10 @@ typedef struct {
   int32_t action_dim, state_dim, max_horizon, max_samples;
   int32_t dtype;   /* cem_dtype: CEM_F32 = fp32 everywhere; CEM_BF16 = bf16
                       weights and activations, fp32 accumulation, LayerNorm
-                      statistics, softmax and energies */
+                      statistics, softmax and energies; the LayerNorm before
+                      q|k|v and before the MLP is folded into those projections
+                      (gain into the weights, shift into the bias, row mean and
+                      rstd applied around the contraction) */
   float ln_eps;
 } cem_model_desc;
 
@@ -102,7 +105,8 @@ const char* cem_last_error(void);
 cem_status cem_weights_count(const cem_model_desc* desc, size_t* n_floats);
 
 /* Create a model on `device`: converts the host fp32 weights to the model
- * dtype (round to nearest even for bf16), lays them out for the kernels,
+ * dtype (round to nearest even for bf16; for CEM_BF16 the LayerNorm gains are
+ * multiplied into the following weights before rounding), lays them out for the kernels,
  * uploads them and allocates the workspace for max_samples x max_horizon
  * (including the KV cache).  Synchronous.  *out receives the handle. */
 cem_status cem_model_create(const cem_model_desc* desc, const float* host_weights,
