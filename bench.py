@@ -267,8 +267,8 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        eprint("bench.py measures one GPU: the plan step runs on a single MI355X; "
-               "multi-GPU runs are not part of this build (--gpus must be 1).")
+        eprint("bench.py measures one GPU: the plan step runs on a single MI355X, and "
+               "several GPUs are not supported (--gpus must be 1).")
         return 2
 
     import numpy as np
