@@ -167,6 +167,24 @@ def plan_roofline_ms(m, pc, peak_tflops: float) -> float:
     return (total + R * per_round) * 1e3
 
 
+def host_cpu():
+    """(CPU model name, logical CPUs this process may run on)."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    return model, avail
+
+
 def cpu_baseline(wl, sample_seconds: float):
     """Time the oracle on the host: whole candidates through the predictor + energy,
     then the per-round search bookkeeping, extrapolated to candidate-evals/s."""
@@ -219,8 +237,9 @@ def cpu_baseline(wl, sample_seconds: float):
         o_refit.refit(xr, el)
     t_book = time.perf_counter() - t1
     plan_s = pc.n_samples * pc.rounds / evals_per_s + t_book
+    cpu_model, host_cpus = host_cpu()
     return {"value": round(evals_per_s, 6), "unit": "candidate-evals/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "host_cpus": host_cpus,
             "one_core_value": round(one_core, 6) if one_core else None,
             "sample": (f"{done} candidate rollouts + L1 energies of the {wl.name} workload in "
                        f"{t_eval:.1f} s (NumPy float64), plus one plan's sampling/top-K/refit "

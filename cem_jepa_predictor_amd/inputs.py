@@ -102,6 +102,11 @@ WORKLOADS: Dict[str, Workload] = {
     # The small case with the fp8 (e4m3) q|k|v and MLP-up projections.
     "small_fp8": Workload("small_fp8", ModelConfig("small_fp8", 6, 512, 8, 2048, 64, 512, "fp8", 3),
                           PlanConfig(256, 32, 5, 3)),
+    # One layer of the small shape with the fp8 projections, horizon 1: shallow
+    # enough that the e4m3 quantization, not the bf16 activation rounding, sets the
+    # difference from the plain model.
+    "shallow_fp8": Workload("shallow_fp8", ModelConfig("shallow_fp8", 1, 512, 8, 2048, 64, 512, "fp8", 1),
+                            PlanConfig(16, 4, 2, 1)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
     # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.

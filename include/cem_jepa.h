@@ -62,9 +62,20 @@ typedef enum {
 typedef enum { CEM_F32 = 0, CEM_BF16 = 1, CEM_FP8 = 2 } cem_dtype;
 
 /* Predictor shape.  Frame block = 1 action token + 1 state token + `patches`
- * frame tokens (B = patches + 2).  d_model % heads == 0, head dim <= 128;
- * d_model, d_mlp and enc_dim must be multiples of 64.  `max_samples` and
- * `max_horizon` size the workspace allocated at create time. */
+ * frame tokens (B = patches + 2).  `max_samples` and `max_horizon` size the
+ * workspace allocated at create time.  Limits (cem_model_create and
+ * cem_weights_count return CEM_E_SHAPE otherwise):
+ *  - d_model one of 128, 256, 384, 512, 768, 1024, 1536, 2048, 4096, and a
+ *    multiple of heads;
+ *  - head dim d_model / heads: exactly 64 for CEM_BF16 and CEM_FP8 models;
+ *    16, 32, 64 or 128 for CEM_F32 models;
+ *  - CEM_BF16 / CEM_FP8: patches + 2 <= 320 (one frame block's keys fit the
+ *    attention kernel's LDS); CEM_FP8 also needs d_model % 512 == 0;
+ *  - d_mlp and enc_dim multiples of 64 in [64, 65536]; patches in [1, 4096];
+ *  - layers in [1, 256]; action_dim and state_dim in [1, 32], equal when
+ *    max_horizon > 1 (the state advances by the action);
+ *  - max_horizon in [1, 8]; max_samples in [1, 16384]; ln_eps > 0, finite;
+ *  - max_samples * (patches + 2) <= 2^30 rows. */
 typedef struct {
   int32_t layers, d_model, heads, d_mlp, patches, enc_dim;
   int32_t action_dim, state_dim, max_horizon, max_samples;

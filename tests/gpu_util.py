@@ -28,9 +28,16 @@ def to_np(t) -> np.ndarray:
     return t.cpu().numpy()
 
 
+def workload(name: str):
+    """A named workload; "sweep_<N>" is the batch-sweep point with N candidates."""
+    if name.startswith("sweep_"):
+        return inputs.sweep_workload(int(name[len("sweep_"):]))
+    return inputs.WORKLOADS[name]
+
+
 @functools.lru_cache(maxsize=None)
 def workload_data(name: str):
-    wl = inputs.WORKLOADS[name]
+    wl = workload(name)
     m = wl.model
     w = inputs.make_weights(m, wl.weight_seed)
     z_obs, z_goal, s0 = inputs.make_embeddings(m, wl.embed_seed)
@@ -65,12 +72,15 @@ def release_models():
 
 def run_plan(name: str, *, use_graph: bool = True, rounds: int | None = None,
              n: int | None = None, k: int | None = None, seed: int | None = None,
-             plan_id: int = 0, horizon: int | None = None, mu_init=None, sigma_init=None):
+             plan_id: int = 0, horizon: int | None = None, mu_init=None, sigma_init=None,
+             z_goal=None):
     """Run cem_plan on the GPU and return outputs and the full trace as numpy.
-    mu_init / sigma_init [H, A] replace the fresh Gaussian when given."""
+    mu_init / sigma_init [H, A] replace the fresh Gaussian when given; z_goal [P, E]
+    replaces the workload's goal embedding."""
     import torch
 
-    wl, _, _, z_obs, z_goal, s0 = workload_data(name)
+    wl, _, _, z_obs, wl_goal, s0 = workload_data(name)
+    z_goal = wl_goal if z_goal is None else np.asarray(z_goal, np.float32)
     pc = wl.plan
     N, K = n or pc.n_samples, k or pc.n_elites
     R, H = rounds or pc.rounds, horizon or pc.horizon
