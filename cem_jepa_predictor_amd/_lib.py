@@ -25,7 +25,7 @@ STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYP
                 -4: "CEM_E_OOM", -5: "CEM_E_HIP", -6: "CEM_E_INTERNAL"}
 
 EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
-           "cem_plan", "cem_plan_batched", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
+           "cem_plan", "cem_plan_batched", "cem_plan_noalloc", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
            "cem_sample", "topk_select", "cem_warm_start", "cem_fp8_quantize_rows", "cem_timer_enable", "cem_timer_read",
            "cem_mfma_ceiling"]
 
@@ -81,6 +81,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cem_model_destroy": [P],
         "cem_plan": [P, ctypes.POINTER(Params), P, P, P, P, P, P, P, P],
         "cem_plan_batched": [P, ctypes.POINTER(Params), I32, P, P, P, P, P, P, P, P],
+        "cem_plan_noalloc": [P, ctypes.POINTER(Params), P, P, P, P, P, P, P, P],
         "cem_plan_trace": [P, I32, P, SZ, P],
         "predictor_rollout": [P, P, I32, I32, P, P, P, P],
         "energy_l1": [P, I32, P, I32, I32, I32, P, P],
@@ -237,7 +238,11 @@ class Model:
 
     def plan(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
              n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,
-             clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True, stream=None):
+             clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True, stream=None,
+             noalloc: bool = False):
+        """cem_plan (or, with noalloc, cem_plan_noalloc: the plan state in the library's
+        per-device scratch, nothing allocated, kernels enqueued directly, the model's
+        trace untouched)."""
         c = self.cfg
         pe, ha = (c.patches, c.enc_dim), (horizon, c.action_dim)
         ptrs = _args((z_obs, "z_obs", _f32(), pe), (z_goal, "z_goal", _f32(), pe),
@@ -247,8 +252,11 @@ class Model:
         p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
                    1 if use_graph else 0)
         with _OnStream(stream) as st:
-            _check(load().cem_plan(self.handle, ctypes.byref(p), *ptrs, st))
-        self._last = p
+            if noalloc:
+                _check(load().cem_plan_noalloc(self.handle, ctypes.byref(p), *ptrs, st))
+            else:
+                _check(load().cem_plan(self.handle, ctypes.byref(p), *ptrs, st))
+                self._last = p
 
     def plan_batched(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
                      n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,

@@ -61,7 +61,7 @@ cem_status check_hip(hipError_t e, const char* what) {
 namespace {
 cem_status plan_checked(cem_model* model, const cem_params* p, int32_t batch, const float* z_obs,
                         const float* z_goal, const float* s0, float* mu, float* sigma, float* action,
-                        int32_t* best_idx, void* stream) {
+                        int32_t* best_idx, void* stream, bool noalloc = false) {
   if (!model || !p || !z_obs || !z_goal || !s0 || !mu || !sigma || !action)
     return fail(CEM_E_ARG, "null argument");
   if (!aligned(z_obs, 4) || !aligned(z_goal, 4) || !aligned(s0, 4) || !aligned(mu, 4) ||
@@ -81,6 +81,9 @@ cem_status plan_checked(cem_model* model, const cem_params* p, int32_t batch, co
   if (p->use_graph != 0 && p->use_graph != 1) return fail(CEM_E_ARG, "use_graph must be 0 or 1");
   if ((uint64_t)p->plan_id + (uint64_t)(batch - 1) > 0xffffffffull)
     return fail(CEM_E_ARG, "plan_id + batch - 1 must fit in 32 bits");
+  if (noalloc)
+    return finish(cem::plan_noalloc(model, *p, z_obs, z_goal, s0, mu, sigma, action, best_idx,
+                                    static_cast<hipStream_t>(stream)));
   return finish(cem::plan(model, *p, batch, z_obs, z_goal, s0, mu, sigma, action, best_idx,
                           static_cast<hipStream_t>(stream)));
 }
@@ -139,6 +142,14 @@ cem_status cem_plan_batched(cem_model* model, const cem_params* p, int32_t batch
                             float* action, int32_t* best_idx, void* stream) {
   return guarded([&]() -> cem_status {
     return plan_checked(model, p, batch, z_obs, z_goal, s0, mu, sigma, action, best_idx, stream);
+  });
+}
+
+cem_status cem_plan_noalloc(cem_model* model, const cem_params* p, const float* z_obs,
+                            const float* z_goal, const float* s0, float* mu, float* sigma,
+                            float* action, int32_t* best_idx, void* stream) {
+  return guarded([&]() -> cem_status {
+    return plan_checked(model, p, 1, z_obs, z_goal, s0, mu, sigma, action, best_idx, stream, true);
   });
 }
 

@@ -15,10 +15,18 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
 #include "model.hpp"
+
+// Plan state of cem_plan_noalloc: one copy of this array on every device the
+// library runs on, for callers that cannot allocate.  In host code `scratch`
+// names a host-side stand-in, not a device address; the address of a device's
+// copy comes from hipGetSymbolAddress, taken once per device when a model is
+// created there (scratch_setup below), and only that address is used.
+static __device__ __align__(256) uint8_t scratch[cem::kPlanScratchBytes];
 
 namespace cem {
 
@@ -81,6 +89,64 @@ struct Layout {
     return o;
   }
 };
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxScratchDevices] = {};
+
+// Record the current device's copy of `scratch` (the device must be current).
+hipError_t scratch_setup(int device) {
+  if (device < 0 || device >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[device]) return hipSuccess;
+  void* ptr = nullptr;
+  const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+  if (e != hipSuccess) return e;
+  if (!ptr) return hipErrorInvalidSymbol;
+  g_scratch[device] = ptr;
+  return hipSuccess;
+}
+
+void* scratch_of(int device) {
+  if (device < 0 || device >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  return g_scratch[device];
+}
+
+// Offsets of the plan state for n candidates, k elites, r rounds, ha = H * A,
+// nb problems, carved from one block of device memory.
+struct PlanLayout {
+  size_t x, e, mu, sg, el, zo, zg, s0, zt, f0, pp, bytes;
+};
+
+PlanLayout plan_layout(const cem_model* m, int n, int k, int r, int ha, int nb) {
+  const size_t P = m->desc.patches, PE = P * m->desc.enc_dim, PD = P * m->desc.d_model;
+  Layout l;
+  PlanLayout o;
+  o.x = l.take((size_t)r * nb * n * ha * 4);
+  o.e = l.take((size_t)r * nb * n * 4);
+  o.mu = l.take((size_t)(r + 1) * nb * ha * 4);
+  o.sg = l.take((size_t)(r + 1) * nb * ha * 4);
+  o.el = l.take((size_t)r * nb * k * 4);
+  o.zo = l.take(nb * PE * 4);
+  o.zg = l.take(nb * PE * 4);
+  o.s0 = l.take((size_t)nb * 64 * 4);
+  o.zt = l.take(nb * PE * m->esz);
+  o.f0 = l.take(nb * PD * m->esz);
+  o.pp = l.take(16);
+  o.bytes = l.off;
+  return o;
+}
+
+void carve_plan_state(PlanState& ps, void* base, const PlanLayout& o) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  ps.x_hist = (float*)(b + o.x); ps.e_hist = (float*)(b + o.e);
+  ps.mu_hist = (float*)(b + o.mu); ps.sigma_hist = (float*)(b + o.sg);
+  ps.elites = (int*)(b + o.el);
+  ps.zobs = (float*)(b + o.zo); ps.zgoal = (float*)(b + o.zg); ps.s0 = (float*)(b + o.s0);
+  ps.zobs_t = b + o.zt; ps.f0 = b + o.f0;
+  ps.params = (uint32_t*)(b + o.pp);
+}
 
 }  // namespace
 
@@ -311,6 +377,8 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   if (e != hipSuccess) return fail(hip_status(e, "gemm_init"));
   e = attention_init();
   if (e != hipSuccess) return fail(hip_status(e, "attention_init"));
+  e = scratch_setup(device);
+  if (e != hipSuccess) return fail(hip_status(e, "hipGetSymbolAddress(scratch)"));
   e = hipStreamCreateWithFlags(&m->cap_stream, hipStreamNonBlocking);
   if (e != hipSuccess) return fail(hip_status(e, "hipStreamCreate"));
   *out = m;
@@ -485,8 +553,8 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
 }
 
 template <typename T>
-hipError_t enqueue_plan_body(cem_model* m, const cem_params& p, int batch, hipStream_t st) {
-  PlanState& ps = m->plan;
+hipError_t enqueue_plan_body(cem_model* m, const PlanState& ps, const cem_params& p, int batch,
+                             hipStream_t st) {
   const int N = p.n_samples, K = p.n_elites, H = p.horizon, ha = H * m->desc.action_dim;
   const int NB = batch * N;
   const long long pe = (long long)m->desc.patches * m->desc.enc_dim;
@@ -518,33 +586,22 @@ Status ensure_plan_state(cem_model* m, const cem_params& p, int batch) {
     return Status::Ok();
   const int n = std::max(p.n_samples, ps.n), k = std::max(p.n_elites, ps.k);
   const int r = std::max(p.rounds, ps.r), hh = std::max(ha, ps.ha), nb = std::max(batch, ps.batch);
-  const size_t P = m->desc.patches, PE = P * m->desc.enc_dim, PD = P * m->desc.d_model;
-  Layout l;
-  const size_t o_x = l.take((size_t)r * nb * n * hh * 4), o_e = l.take((size_t)r * nb * n * 4);
-  const size_t o_mu = l.take((size_t)(r + 1) * nb * hh * 4), o_sg = l.take((size_t)(r + 1) * nb * hh * 4);
-  const size_t o_el = l.take((size_t)r * nb * k * 4);
-  const size_t o_zo = l.take(nb * PE * 4), o_zg = l.take(nb * PE * 4), o_s0 = l.take((size_t)nb * 64 * 4);
-  const size_t o_zt = l.take(nb * PE * m->esz), o_f0 = l.take(nb * PD * m->esz), o_pp = l.take(16);
+  const PlanLayout l = plan_layout(m, n, k, r, hh, nb);
   // existing graphs reference the old buffers
   CEM_TRY(hipDeviceSynchronize(), "hipDeviceSynchronize");
   for (auto& kv : m->graphs) (void)hipGraphExecDestroy(kv.second);
   m->graphs.clear();
   if (ps.mem) { (void)hipFree(ps.mem); ps.mem = nullptr; }
-  CEM_TRY(hipMalloc(&ps.mem, l.off), "hipMalloc(plan state)");
-  uint8_t* b = static_cast<uint8_t*>(ps.mem);
+  CEM_TRY(hipMalloc(&ps.mem, l.bytes), "hipMalloc(plan state)");
   ps.n = n; ps.k = k; ps.r = r; ps.ha = hh; ps.batch = nb;
-  ps.x_hist = (float*)(b + o_x); ps.e_hist = (float*)(b + o_e);
-  ps.mu_hist = (float*)(b + o_mu); ps.sigma_hist = (float*)(b + o_sg);
-  ps.elites = (int*)(b + o_el);
-  ps.zobs = (float*)(b + o_zo); ps.zgoal = (float*)(b + o_zg); ps.s0 = (float*)(b + o_s0);
-  ps.zobs_t = b + o_zt; ps.f0 = b + o_f0;
-  ps.params = (uint32_t*)(b + o_pp);
+  carve_plan_state(ps, ps.mem, l);
   return Status::Ok();
 }
 
 template <typename T>
 Status run_plan(cem_model* m, const cem_params& p, int batch, hipStream_t st) {
-  if (!p.use_graph || m->timers) return hip_status(enqueue_plan_body<T>(m, p, batch, st), "plan kernels");
+  const PlanState& ps = m->plan;
+  if (!p.use_graph || m->timers) return hip_status(enqueue_plan_body<T>(m, ps, p, batch, st), "plan kernels");
   uint32_t lo_bits, hi_bits;
   std::memcpy(&lo_bits, &p.clamp_lo, 4);
   std::memcpy(&hi_bits, &p.clamp_hi, 4);
@@ -552,7 +609,7 @@ Status run_plan(cem_model* m, const cem_params& p, int batch, hipStream_t st) {
   auto it = m->graphs.find(key);
   if (it == m->graphs.end()) {
     CEM_TRY(hipStreamBeginCapture(m->cap_stream, hipStreamCaptureModeThreadLocal), "hipStreamBeginCapture");
-    const hipError_t body = enqueue_plan_body<T>(m, p, batch, m->cap_stream);
+    const hipError_t body = enqueue_plan_body<T>(m, ps, p, batch, m->cap_stream);
     hipGraph_t g = nullptr;
     const hipError_t end = hipStreamEndCapture(m->cap_stream, &g);
     if (body != hipSuccess) { if (g) (void)hipGraphDestroy(g); return hip_status(body, "plan capture"); }
@@ -583,13 +640,12 @@ Status rollout(cem_model* m, const float* actions, int n, int horizon, const flo
   return Status::Ok();
 }
 
-Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, const float* z_goal,
-            const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
-            hipStream_t st) {
-  DeviceGuard guard(m->device);
-  Status s = ensure_plan_state(m, p, batch);
-  if (!s.ok()) return s;
-  PlanState& ps = m->plan;
+namespace {
+
+// Inputs into the plan state, the rounds (graph replay or direct enqueue), results out.
+Status plan_with_state(cem_model* m, const PlanState& ps, bool direct, const cem_params& p, int batch,
+                       const float* z_obs, const float* z_goal, const float* s0, float* mu,
+                       float* sigma, float* action, int32_t* best_idx, hipStream_t st) {
   const size_t PE = (size_t)m->desc.patches * m->desc.enc_dim, S = m->desc.state_dim;
   const int A = m->desc.action_dim, ha = p.horizon * A, K = p.n_elites;
   const size_t nb = (size_t)batch;
@@ -599,7 +655,12 @@ Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, co
   CEM_TRY(hipMemcpyAsync(ps.mu_hist, mu, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy mu");
   CEM_TRY(hipMemcpyAsync(ps.sigma_hist, sigma, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma");
   CEM_TRY(launch_set_params(ps.params, p.seed, p.plan_id, st), "set params");
-  s = m->bf16 ? run_plan<bf16>(m, p, batch, st) : run_plan<float>(m, p, batch, st);
+  Status s;
+  if (direct)
+    s = hip_status(m->bf16 ? enqueue_plan_body<bf16>(m, ps, p, batch, st)
+                           : enqueue_plan_body<float>(m, ps, p, batch, st), "plan kernels");
+  else
+    s = m->bf16 ? run_plan<bf16>(m, p, batch, st) : run_plan<float>(m, p, batch, st);
   if (!s.ok()) return s;
   const float* mu_r = ps.mu_hist + (size_t)p.rounds * nb * ha;
   const float* sg_r = ps.sigma_hist + (size_t)p.rounds * nb * ha;
@@ -611,9 +672,51 @@ Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, co
   if (best_idx)
     CEM_TRY(hipMemcpy2DAsync(best_idx, 4, ps.elites + (size_t)(p.rounds - 1) * nb * K, (size_t)K * 4, 4, nb,
                              hipMemcpyDeviceToDevice, st), "copy best_idx");
+  return Status::Ok();
+}
+
+}  // namespace
+
+Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, const float* z_goal,
+            const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
+            hipStream_t st) {
+  DeviceGuard guard(m->device);
+  Status s = ensure_plan_state(m, p, batch);
+  if (!s.ok()) return s;
+  PlanState& ps = m->plan;
+  s = plan_with_state(m, ps, false, p, batch, z_obs, z_goal, s0, mu, sigma, action, best_idx, st);
+  if (!s.ok()) return s;
   ps.last_n = p.n_samples; ps.last_k = p.n_elites; ps.last_r = p.rounds; ps.last_h = p.horizon;
   ps.last_batch = batch;
   return Status::Ok();
+}
+
+Status plan_noalloc(cem_model* m, const cem_params& p, const float* z_obs, const float* z_goal,
+                    const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
+                    hipStream_t st) {
+  DeviceGuard guard(m->device);
+  Status bad;
+  if (m->timers) {
+    bad.code = CEM_E_ARG;
+    bad.msg = "cem_plan_noalloc: kernel timers are enabled on this model (they record events)";
+    return bad;
+  }
+  const PlanLayout l = plan_layout(m, p.n_samples, p.n_elites, p.rounds, p.horizon * m->desc.action_dim, 1);
+  if (l.bytes > kPlanScratchBytes) {
+    bad.code = CEM_E_SHAPE;
+    bad.msg = "cem_plan_noalloc: the plan state needs " + std::to_string(l.bytes) +
+              " bytes, more than the " + std::to_string(kPlanScratchBytes) + "-byte scratch";
+    return bad;
+  }
+  void* base = scratch_of(m->device);
+  if (!base) {
+    bad.code = CEM_E_INTERNAL;
+    bad.msg = "cem_plan_noalloc: no scratch address for this device";
+    return bad;
+  }
+  PlanState ps;
+  carve_plan_state(ps, base, l);
+  return plan_with_state(m, ps, true, p, 1, z_obs, z_goal, s0, mu, sigma, action, best_idx, st);
 }
 
 Status plan_trace(cem_model* m, int kind, void* dst, size_t bytes, hipStream_t st) {

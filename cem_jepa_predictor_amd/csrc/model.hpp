@@ -13,6 +13,9 @@
 
 namespace cem {
 
+// Bytes of the per-device plan-state scratch behind cem_plan_noalloc.
+constexpr size_t kPlanScratchBytes = size_t(8) << 20;
+
 struct Status {
   cem_status code = CEM_OK;
   std::string msg;
@@ -112,6 +115,12 @@ Status rollout(cem_model* m, const float* actions, int n, int horizon, const flo
 Status plan(cem_model* m, const cem_params& p, int batch, const float* z_obs, const float* z_goal,
             const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
             hipStream_t st);
+// The single-problem plan with its plan state in the device's `scratch` array
+// (kPlanScratchBytes): no allocation, kernels enqueued directly, the model's
+// trace left untouched.
+Status plan_noalloc(cem_model* m, const cem_params& p, const float* z_obs, const float* z_goal,
+                    const float* s0, float* mu, float* sigma, float* action, int32_t* best_idx,
+                    hipStream_t st);
 Status plan_trace(cem_model* m, int kind, void* dst, size_t bytes, hipStream_t st);
 Status timer_read(cem_model* m, int64_t* launches, double* ms, double* flop);
 

@@ -160,6 +160,31 @@ cem_status cem_plan_batched(cem_model* model, const cem_params* params, int32_t 
                             const float* z_obs, const float* z_goal, const float* s0, float* mu,
                             float* sigma, float* action, int32_t* best_idx, void* stream);
 
+/* cem_plan without allocation, for callers that cannot call hipMalloc: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation.
+ * Arguments, results and errors are those of cem_plan, and the results are
+ * bitwise equal to cem_plan's for the same arguments.  Differences:
+ *  - The plan state (per-round samples, energies, elites and Gaussians, the
+ *    staged z_obs / z_goal / s0 and the frame-0 tokens) lives in a static device
+ *    array of 8 MiB (8388608 bytes) that the library holds on each device it runs
+ *    on until the process ends.  Bytes needed, each term rounded up to 256:
+ *    R N H A 4 + R N 4 + 2 (R + 1) H A 4 + R K 4 + 2 P E 4 + 256 + P E es + P d es
+ *    + 16, with es = 4 for CEM_F32 and 2 otherwise (the 800 x 10 plan at the
+ *    V-JEPA2-AC shape needs about 4.4 MB).  A plan that needs more returns
+ *    CEM_E_SHAPE and enqueues nothing.
+ *  - Every call on a device shares that device's array: calls that overlap on
+ *    one GPU (two streams, or two models on one device) race and corrupt each
+ *    other.  The array keeps the last call's contents; nothing in it needs to
+ *    start at zero.
+ *  - Kernels and copies are enqueued directly on `stream` (params->use_graph is
+ *    ignored), so a caller may capture them into its own graph.  The model's
+ *    workspace (allocated by cem_model_create) is used as by cem_plan.
+ *  - cem_plan_trace keeps describing the last cem_plan, not this call.
+ *  - Kernel timers must be off on the model (CEM_E_ARG otherwise). */
+cem_status cem_plan_noalloc(cem_model* model, const cem_params* params, const float* z_obs,
+                            const float* z_goal, const float* s0, float* mu, float* sigma,
+                            float* action, int32_t* best_idx, void* stream);
+
 typedef enum {
   CEM_TRACE_ACTIONS = 0,  /* fp32 [R, N, H, A] sampled candidates */
   CEM_TRACE_ENERGY = 1,   /* fp32 [R, N] energies */
