@@ -87,9 +87,11 @@ def summarize_stats(path: str, top: int = 12) -> None:
 
 
 def summarize_traffic(fetch: str, write: str, copy_fetch: str, copy_write: str,
-                      copy_bytes: int) -> None:
+                      copy_bytes: int, stats: str | None = None) -> None:
     """Per-kernel FETCH_SIZE / WRITE_SIZE means (KiB per dispatch) of two
-    rocprofv3 --pmc passes, scaled by the copy calibration."""
+    rocprofv3 --pmc passes, scaled by the copy calibration; with the
+    --kernel-trace --stats CSV of the same command, also each kernel's mean
+    duration and the HBM-side GB/s it reaches."""
     import collections
     import csv
 
@@ -108,14 +110,25 @@ def summarize_traffic(fetch: str, write: str, copy_fetch: str, copy_write: str,
     ff, fw = kib / copy_mean(copy_fetch), kib / copy_mean(copy_write)
     print(f"copy calibration ({copy_bytes} bytes): FETCH_SIZE x {ff:.4f}, WRITE_SIZE x {fw:.4f}\n")
     df, dw = per_kernel(fetch), per_kernel(write)
-    print("| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes / dispatch |")
-    print("|---|---:|---:|---:|---:|")
+    short = lambda k: k.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")  # noqa: E731
+    avg_ns = {}
+    if stats:
+        for r in csv.DictReader(open(stats)):
+            avg_ns[short(r["Name"])] = float(r["AverageNs"])
+    print("| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | scaled bytes / dispatch"
+          + (" | mean duration (us) | HBM-side GB/s |" if stats else " |"))
+    print("|---|---:|---:|---:|---:|" + ("---:|---:|" if stats else ""))
     keys = sorted(df, key=lambda k: -sum(df[k]))
-    for k in keys[:10]:
+    for k in keys:
         f = sum(df[k]) / len(df[k])
         w = sum(dw.get(k, [0.0])) / max(len(dw.get(k, [])), 1)
-        name = k.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
-        print(f"| `{name}` | {len(df[k])} | {f:.1f} | {w:.1f} | {(f * ff + w * fw) * 1024:.4g} |")
+        name = short(k)
+        b = (f * ff + w * fw) * 1024
+        row = f"| `{name}` | {len(df[k])} | {f:.1f} | {w:.1f} | {b:.4g} |"
+        if stats:
+            ns = avg_ns.get(name)
+            row += f" {ns / 1e3:.1f} | {b / ns:.0f} |" if ns else " - | - |"
+        print(row)
     gf = [x for k, xs in df.items() if "gemm_bf16_kernel" in k for x in xs]
     gw = [x for k, xs in dw.items() if "gemm_bf16_kernel" in k for x in xs]
     if gf and gw:
@@ -272,16 +285,21 @@ def main() -> int:
                          "(reference for rocprofv3 FETCH_SIZE / WRITE_SIZE) and exit")
     ap.add_argument("--summarize-stats", metavar="KERNEL_STATS_CSV",
                     help="print a markdown summary of a rocprofv3 --stats CSV and exit")
-    ap.add_argument("--summarize-traffic", nargs=4,
-                    metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="print per-kernel HBM bytes from rocprofv3 --pmc CSVs (FETCH_SIZE, "
-                         "WRITE_SIZE of the bench; the same of the --copy-bytes run) and exit")
+    ap.add_argument("--summarize-traffic", nargs="+",
+                    metavar="CSV",
+                    help="print per-kernel HBM bytes from rocprofv3 --pmc CSVs: FETCH_SIZE, "
+                         "WRITE_SIZE of the bench, the same of the --copy-bytes run, and "
+                         "optionally the --kernel-trace --stats CSV of the bench (mean duration, "
+                         "GB/s), then exit")
     args = ap.parse_args()
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
         return 0
     if args.summarize_traffic:
-        summarize_traffic(*args.summarize_traffic, copy_bytes=args.copy_bytes or (1 << 30))
+        if len(args.summarize_traffic) not in (4, 5):
+            ap.error("--summarize-traffic takes 4 or 5 CSV paths")
+        summarize_traffic(*args.summarize_traffic[:4], copy_bytes=args.copy_bytes or (1 << 30),
+                          stats=(args.summarize_traffic[4:] or [None])[0])
         return 0
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -9,12 +9,20 @@
 // accumulated in float64 in elite order, rounded to float32.
 //
 // One 1024-thread workgroup: a bitonic sort of the padded key array in LDS
-// (n <= 16384 keys = 128 KB), then the first k keys give the elites.  The
-// whole step is a few microseconds: it is launch-latency bound.
+// (n <= 16384 keys = 128 KB), then the first k keys give the elites.  The refit
+// spreads the gather of the elites' samples over the whole workgroup: for
+// h * a <= 1024, P = 1024 / (h * a) threads per (step, action dim) each sum the
+// elites P apart, and the P partial sums are added in a fixed order (float64
+// throughout), so the result is deterministic.  The whole step is a few
+// microseconds: it is launch-latency bound.
 #include "kernels.hpp"
 
 namespace cem {
 namespace {
+
+constexpr int kRefitThreads = 1024;   // the workgroup; also the partial-sum slots
+// LDS beyond the keys: kRefitThreads partial sums and up to kRefitThreads means
+constexpr int kRefitLds = 2 * kRefitThreads * (int)sizeof(double);
 
 __device__ __forceinline__ uint64_t select_key(float e, int i) {
   uint32_t u = __float_as_uint(e);
@@ -24,7 +32,7 @@ __device__ __forceinline__ uint64_t select_key(float e, int i) {
   return ((uint64_t)ord << 32) | (uint32_t)i;
 }
 
-__global__ __launch_bounds__(1024) void select_refit_kernel(const float* __restrict__ E,
+__global__ __launch_bounds__(kRefitThreads) void select_refit_kernel(const float* __restrict__ E,
                                                             const float* __restrict__ X, int n,
                                                             int npad, int k, int ha,
                                                             int* __restrict__ idx,
@@ -53,7 +61,41 @@ __global__ __launch_bounds__(1024) void select_refit_kernel(const float* __restr
     }
   }
   for (int i = tid; i < k; i += blockDim.x) idx[i] = (int)(uint32_t)keys[i];
-  if (mu) {
+  if (mu && ha <= kRefitThreads) {
+    // LDS after the keys: P x ha partial sums, then ha means (float64)
+    double* part = reinterpret_cast<double*>(keys + npad);
+    double* mean = part + kRefitThreads;
+    const int P = kRefitThreads / ha, j = tid % ha, prt = tid / ha;
+    auto xel = [&](int i) { return (double)X[(long long)(uint32_t)keys[i] * ha + j]; };
+    if (prt < P) {
+      double s = 0.0;
+      for (int i = prt; i < k; i += P) s += xel(i);
+      part[prt * ha + j] = s;
+    }
+    __syncthreads();
+    if (tid < ha) {
+      double s = 0.0;
+      for (int q = 0; q < P; ++q) s += part[q * ha + tid];
+      mean[tid] = s / (double)k;
+    }
+    __syncthreads();
+    if (prt < P) {
+      const double m = mean[j];
+      double v = 0.0;
+      for (int i = prt; i < k; i += P) {
+        const double dlt = xel(i) - m;
+        v += dlt * dlt;
+      }
+      part[prt * ha + j] = v;
+    }
+    __syncthreads();
+    if (tid < ha) {
+      double v = 0.0;
+      for (int q = 0; q < P; ++q) v += part[q * ha + tid];
+      mu[tid] = (float)mean[tid];
+      sigma[tid] = (float)sqrt(v / (double)k);
+    }
+  } else if (mu) {
     for (int j = tid; j < ha; j += blockDim.x) {
       double s = 0.0;
       for (int i = 0; i < k; ++i) s += (double)X[(long long)(uint32_t)keys[i] * ha + j];
@@ -107,7 +149,7 @@ hipError_t launch_warm_start(const float* mu_prev, const float* sigma_prev, int 
 hipError_t select_init() {
   return hipFuncSetAttribute(reinterpret_cast<const void*>(&select_refit_kernel),
                              hipFuncAttributeMaxDynamicSharedMemorySize,
-                             kMaxSelect * (int)sizeof(uint64_t));
+                             kMaxSelect * (int)sizeof(uint64_t) + kRefitLds);
 }
 
 hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int ha, int* idx,
@@ -115,8 +157,8 @@ hipError_t launch_select_refit(const float* E, const float* X, int n, int k, int
   if (n <= 0 || k <= 0 || batch <= 0) return hipSuccess;
   int npad = 2;
   while (npad < n) npad <<= 1;
-  select_refit_kernel<<<batch, 1024, npad * sizeof(uint64_t), stream>>>(E, X, n, npad, k, ha, idx, mu,
-                                                                      sigma);
+  const size_t lds = npad * sizeof(uint64_t) + (mu ? kRefitLds : 0);
+  select_refit_kernel<<<batch, kRefitThreads, lds, stream>>>(E, X, n, npad, k, ha, idx, mu, sigma);
   return hipGetLastError();
 }
 

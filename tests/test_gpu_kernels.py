@@ -113,6 +113,26 @@ def test_energy_l1_matches_oracle(gpu_lib, dtype, n, p, e):
     np.testing.assert_allclose(to_np(out), want, rtol=2e-5, atol=0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_energy_l1_is_independent_of_the_batch(gpu_lib, dtype):
+    """A candidate's energy is summed in the same order whether its workgroup scores
+    four candidates (n divisible by 4) or only it: every sub-batch gives the same bits."""
+    import torch
+    from cem_jepa_predictor_amd import _lib, inputs
+
+    zp, zg = inputs.make_predictions(12, 16, 136, seed=5)
+    tz = to_dev(zp)
+    if dtype == "bf16":
+        tz = tz.to(torch.bfloat16)
+    full = torch.empty(12, dtype=torch.float32, device="cuda")
+    _lib.energy_l1(tz, to_dev(zg), full)
+    for lo, hi in ((0, 7), (3, 12), (5, 6), (4, 8)):
+        part = torch.empty(hi - lo, dtype=torch.float32, device="cuda")
+        _lib.energy_l1(tz[lo:hi].contiguous(), to_dev(zg), part)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(part), to_np(full)[lo:hi], err_msg=f"candidates {lo}..{hi - 1}")
+
+
 def test_energy_l1_full_size_sampled(gpu_lib):
     """N=800 candidates of [256, 1408] bf16 predictions, oracle on a sample of rows."""
     import torch
