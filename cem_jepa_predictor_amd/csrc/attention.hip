@@ -49,16 +49,22 @@ constexpr __host__ __device__ int kpad_of(int B) { return (B + 31) & ~31; }
 // K and V of one frame block, row-major, padded to a multiple of 32 keys
 __host__ __device__ __forceinline__ int lds_bytes_of(int B) { return 2 * kpad_of(B) * kDh * 2; }
 
+// Lanes l, l^16, l^32, l^48 share query l % 16.  v_permlane16_swap exchanges the
+// odd 16-lane rows of its first operand with the even rows of its second: with
+// both operands v, the two results hold (v[l], v[l ^ 16]) in some order in every
+// lane, so their max or sum is the xor-16 combination; v_permlane32_swap does the
+// same for the two 32-lane halves.  Plain VALU: no LDS round trip.
 __device__ __forceinline__ float wave_max_q(float v) {
-  // lanes l, l^16, l^32, l^48 share query l % 16
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  v = fmaxf(v, __shfl_xor(v, 32, 64));
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float wave_sum_q(float v) {
-  v += __shfl_xor(v, 16, 64);
-  v += __shfl_xor(v, 32, 64);
-  return v;
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // One frame block (every query sees exactly the B keys of its own block).

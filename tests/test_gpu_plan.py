@@ -498,3 +498,35 @@ def test_energy_ranking_with_reachable_goal(gpu_lib, name, n):
     # 0.9993 on small; at 24 layers it is a larger share of the smaller effect of an
     # action on the predicted frame
     assert stats["reachable goal"] >= (0.999 if name == "small" else 0.99)
+
+
+def test_plan_small_reachable_goal_independent(gpu_lib):
+    """Independent plan, bf16 (page section 01: sample, predict, score, keep the best,
+    refit; execute the first action of the final Gaussian).  The goal is reachable --
+    the oracle's predicted frame for a known action sequence a* -- so the energies
+    carry a real signal; the GPU plans on its own energies and its action must land
+    near the oracle's own float64 plan, stored by tests/golden/make_small_reachable_plan.py.
+    Bound: bf16 storage of the activations alone (emulated on the oracle) moves this
+    plan's action by 0.058 and keeps 28-31 of the 32 elites per round, so the action is
+    held to 0.15 and round 0 (same samples on both sides) to 28 shared elites."""
+    import json
+    import os
+
+    path = os.path.join(os.path.dirname(__file__), "golden", "small_reachable_plan.json")
+    with open(path) as f:
+        rec = json.load(f)
+    from cem_jepa_predictor_amd import inputs
+
+    wl, _, _, z_obs, _, s0 = workload_data("small")
+    pred = oracle_predictor("small")
+    a_star = inputs.make_actions(1, wl.plan.horizon, seed=rec["a_star_seed"]) * np.float32(rec["a_star_scale"])
+    np.testing.assert_array_equal(a_star[0], np.asarray(rec["a_star"], np.float32))
+    goal = pred.rollout_cached(a_star, z_obs, s0)[0].astype(np.float32)
+    out = run_plan("small", z_goal=goal)
+    want = np.asarray(rec["action"], np.float32)
+    diff = float(np.abs(out["action"] - want).max())
+    shared0 = len(set(out["elites"][0].tolist()) & set(rec["elites"][0]))
+    log(f"  action {np.round(out['action'], 3).tolist()} vs oracle {np.round(want, 3).tolist()} "
+        f"(a* first step {np.round(a_star[0, 0], 3).tolist()}): max diff {diff:.3f}; round-0 elites shared {shared0}/32")
+    assert shared0 >= 28
+    assert diff <= 0.15
