@@ -17,6 +17,7 @@ from .inputs import ModelConfig
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libcem_jepa.so")
+PROBE_LIB_PATH = os.path.join(_PKG, "libcem_probe.so")   # measurement only (cem_probe.h)
 
 CEM_F32, CEM_BF16, CEM_FP8 = 0, 1, 2
 _MODEL_DTYPES = {"f32": CEM_F32, "bf16": CEM_BF16, "fp8": CEM_FP8}
@@ -26,8 +27,8 @@ STATUS_NAMES = {0: "CEM_OK", -1: "CEM_E_ARG", -2: "CEM_E_SHAPE", -3: "CEM_E_DTYP
 
 EXPORTS = ["cem_last_error", "cem_weights_count", "cem_model_create", "cem_model_destroy",
            "cem_plan", "cem_plan_batched", "cem_plan_noalloc", "cem_plan_trace", "predictor_rollout", "energy_l1", "elite_refit",
-           "cem_sample", "topk_select", "cem_warm_start", "cem_fp8_quantize_rows", "cem_timer_enable", "cem_timer_read",
-           "cem_mfma_ceiling"]
+           "cem_sample", "topk_select", "cem_warm_start", "cem_fp8_quantize_rows", "cem_timer_enable", "cem_timer_read"]
+PROBE_EXPORTS = ["cem_mfma_ceiling"]
 
 
 class CemError(RuntimeError):
@@ -93,7 +94,6 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "cem_timer_enable": [P, I32],
         "cem_timer_read": [P, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_double),
                            ctypes.POINTER(ctypes.c_double)],
-        "cem_mfma_ceiling": [I32, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)],
     }
     for name, args in sigs.items():
         fn = getattr(lib, name)
@@ -390,10 +390,30 @@ def fp8_quantize_rows(x, codes, scale, stream=None):
         _check(load().cem_fp8_quantize_rows(ptrs[0], r, c, ptrs[1], ptrs[2], st))
 
 
+_probe: Optional[ctypes.CDLL] = None
+
+
+def load_probe(path: str = PROBE_LIB_PATH) -> ctypes.CDLL:
+    """The measurement probe library (raises if it has not been built)."""
+    global _probe
+    if _probe is not None:
+        return _probe
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m cem_jepa_predictor_amd.build`")
+    load()   # same HIP runtime as the plan library (torch's)
+    lib = ctypes.CDLL(path)
+    lib.cem_mfma_ceiling.argtypes = [I32, I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+    lib.cem_mfma_ceiling.restype = ctypes.c_int
+    _probe = lib
+    return lib
+
+
 def mfma_ceiling(random_operands: bool = True, launches: int = 40):
     """Sustained dense bf16 MFMA TFLOP/s and shader clock (MHz) of the current
-    device, register-only (cem_mfma_ceiling); synchronous."""
+    device, register-only (cem_mfma_ceiling in the probe library); synchronous."""
     tf, mhz = ctypes.c_double(), ctypes.c_double()
-    _check(load().cem_mfma_ceiling(1 if random_operands else 0, int(launches), ctypes.byref(tf),
-                                   ctypes.byref(mhz)))
+    st = load_probe().cem_mfma_ceiling(1 if random_operands else 0, int(launches), ctypes.byref(tf),
+                                       ctypes.byref(mhz))
+    if st != 0:
+        raise CemError(st, "cem_mfma_ceiling failed (arguments or HIP runtime)")
     return tf.value, mhz.value

@@ -22,10 +22,13 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_NAME = "libcem_jepa.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
+# the measurement probe (cem_probe.h) is a library of its own
+PROBE_LIB_PATH = os.path.join(PKG, "libcem_probe.so")
 ARCH = "gfx950"
 
 SOURCES = ["sampler.hip", "embed.hip", "layernorm.hip", "gemm.hip", "attention.hip",
-           "energy.hip", "select_refit.hip", "probe.hip", "model.hip", "abi.hip"]
+           "energy.hip", "select_refit.hip", "model.hip", "abi.hip"]
+PROBE_SOURCES = ["probe.hip"]
 NO_CONTRACT = {"sampler.hip", "select_refit.hip"}
 # attention keeps its MFMA accumulators in VGPRs: its softmax rescales them with VALU ops
 EXTRA = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
@@ -57,19 +60,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True, jobs: int = 8) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = True, jobs: int = 8) -> str:
+    """Compile every source and link the plan library and the probe library;
+    returns the plan library's path."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], LIB_PATH)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB_PATH)
     if verbose:
-        print(f"built {LIB_PATH}")
+        print(f"built {LIB_PATH} and {PROBE_LIB_PATH}")
     return LIB_PATH
 
 

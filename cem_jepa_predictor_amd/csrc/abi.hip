@@ -285,14 +285,4 @@ cem_status cem_timer_read(cem_model* model, int64_t* launches, double* total_ms,
   });
 }
 
-cem_status cem_mfma_ceiling(int32_t random_operands, int32_t launches, double* tflops,
-                             double* mhz) {
-  return guarded([&]() -> cem_status {
-    if (!tflops || !mhz) return fail(CEM_E_ARG, "null argument");
-    if (random_operands != 0 && random_operands != 1) return fail(CEM_E_ARG, "random_operands must be 0 or 1");
-    if (launches < 2 || launches > 10000) return fail(CEM_E_ARG, "launches must be in [2, 10000]");
-    return check_hip(cem::mfma_ceiling(random_operands, launches, tflops, mhz), "mfma ceiling probe");
-  });
-}
-
 }  // extern "C"

@@ -116,10 +116,4 @@ hipError_t launch_warm_start(const float* mu_prev, const float* sigma_prev, int 
                              float* sigma_next, hipStream_t stream);
 hipError_t select_init();
 
-// --- probe.hip -------------------------------------------------------------------
-// Sustained bf16 MFMA throughput (TFLOP/s) and shader clock (MHz) on the
-// current device over `launches` launches of a register-only MFMA loop
-// (first half untimed); synchronous.
-hipError_t mfma_ceiling(int random_operands, int launches, double* tflops, double* mhz);
-
 }  // namespace cem

@@ -9,6 +9,7 @@
 // accumulators), no memory traffic inside the timed loop.  One workgroup of
 // four waves per CU.  Each workgroup also records its shader-clock cycles and
 // constant-rate (100 MHz) wall ticks, which give the clock it ran at.
+#include "cem_probe.h"
 #include "kernels.hpp"
 
 namespace cem {
@@ -108,3 +109,11 @@ hipError_t mfma_ceiling(int random_operands, int launches, double* tflops, doubl
 }
 
 }  // namespace cem
+
+extern "C" cem_status cem_mfma_ceiling(int32_t random_operands, int32_t launches, double* tflops,
+                                       double* mhz) {
+  if (!tflops || !mhz) return CEM_E_ARG;
+  if (random_operands != 0 && random_operands != 1) return CEM_E_ARG;
+  if (launches < 2 || launches > 10000) return CEM_E_ARG;
+  return cem::mfma_ceiling(random_operands, launches, tflops, mhz) == hipSuccess ? CEM_OK : CEM_E_HIP;
+}

@@ -268,20 +268,6 @@ cem_status cem_timer_enable(cem_model* model, int32_t enable);
 cem_status cem_timer_read(cem_model* model, int64_t* launches, double* total_ms,
                           double* total_flop);
 
-/* Measurement of the matrix cores' sustained ceiling on the current device:
- * `launches` back-to-back launches (the first half untimed) of a kernel in
- * which every wave issues only v_mfma_f32_32x32x16_bf16 on register-resident
- * operands (one 4-wave workgroup per CU, no memory traffic).  With
- * random_operands = 1 the operand bits are pseudo-random, as real activations
- * and weights are; with 0 they are constant.  Returns the sustained dense bf16
- * TFLOP/s and the shader clock (MHz) the timed launches ran at.  Synchronous;
- * allocates and frees a small device buffer; about 6 ms per launch on MI355X.
- * The dense projections' throughput is reported against the published peak
- * and read next to this figure: under full MFMA load with changing operand
- * bits the part lowers its clock to stay within its power limit. */
-cem_status cem_mfma_ceiling(int32_t random_operands, int32_t launches, double* tflops,
-                            double* mhz);
-
 #ifdef __cplusplus
 }
 #endif

@@ -12,10 +12,11 @@ from cem_jepa_predictor_amd import _lib, inputs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "cem_jepa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "cem_probe.h")
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
 
@@ -35,13 +36,28 @@ def test_header_declares_the_boundary():
     assert set(fns) == set(_lib.EXPORTS)
 
 
-def test_library_exports_every_declared_symbol(lib):
-    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+def _exported(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True,
                          text=True, check=True).stdout
-    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    return {line.split()[-1] for line in out.splitlines() if " T " in line}
+
+
+def test_library_exports_every_declared_symbol(lib):
+    exported = _exported(_lib.LIB_PATH)
     for name in declared_functions():
         assert name in exported, name
         assert hasattr(lib, name)
+
+
+def test_probe_library_exports_its_header_and_the_plan_library_none_of_it(lib):
+    probe = _lib.load_probe()
+    fns = declared_functions(PROBE_HEADER)
+    assert set(fns) == set(_lib.PROBE_EXPORTS)
+    exported = _exported(_lib.PROBE_LIB_PATH)
+    for name in fns:
+        assert name in exported, name
+        assert hasattr(probe, name)
+    assert not set(fns) & _exported(_lib.LIB_PATH)
 
 
 def test_weights_count_matches_canonical_layout(lib):
@@ -126,10 +142,11 @@ def test_plan_calls_validate_null_model(lib):
 
 
 def test_mfma_ceiling_validates_before_launch(lib):
+    probe = _lib.load_probe()
     tf, mhz = ctypes.c_double(), ctypes.c_double()
-    assert lib.cem_mfma_ceiling(1, 1, ctypes.byref(tf), ctypes.byref(mhz)) == -1
-    assert lib.cem_mfma_ceiling(2, 10, ctypes.byref(tf), ctypes.byref(mhz)) == -1
-    assert lib.cem_mfma_ceiling(1, 10, None, ctypes.byref(mhz)) == -1
+    assert probe.cem_mfma_ceiling(1, 1, ctypes.byref(tf), ctypes.byref(mhz)) == -1
+    assert probe.cem_mfma_ceiling(2, 10, ctypes.byref(tf), ctypes.byref(mhz)) == -1
+    assert probe.cem_mfma_ceiling(1, 10, None, ctypes.byref(mhz)) == -1
 
 
 def test_binding_rejects_bad_tensors_before_the_library():
