@@ -430,13 +430,15 @@ def test_rollout_many_tiles_equals_oracle_checked_chunks(gpu_lib, name):
     assert err <= ztol * np.abs(want).max()
 
 
-def test_plan_sweep_3200_lockstep(gpu_lib):
-    """The largest batch-sweep point (3200 candidates, K = 320) for one round: sampler,
-    rollout, energy, selection and refit at M = 825,600 rows, the oracle on 2 candidates."""
-    name = "sweep_3200"
-    log(f"plan {name} 1 round lockstep, oracle on candidates 0 and 3199")
+@pytest.mark.parametrize("n", [200, 1600, 3200])
+def test_plan_sweep_lockstep(gpu_lib, n):
+    """Batch-sweep points (N candidates, K = N / 10) for one round: sampler, rollout,
+    energy, selection and refit at M = 258 N rows (825,600 at N = 3200), the oracle on
+    the first and last candidates."""
+    name = f"sweep_{n}"
+    log(f"plan {name} 1 round lockstep, oracle on candidates 0 and {n - 1}")
     out = run_plan(name, rounds=1)
-    worst = _lockstep(name, out, lambda r, n: np.array([0, n - 1]))
+    worst = _lockstep(name, out, lambda r, nn: np.array([0, nn - 1]))
     log(f"  worst energy rel err {worst:.3e}")
     release_models()
 
