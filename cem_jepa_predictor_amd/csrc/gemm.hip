@@ -41,8 +41,8 @@
 //    results are stored; no tile pays a prologue.
 //  * Tile order is XCD-aware: the dispatcher hands workgroup b to XCD b % 8;
 //    each XCD owns a contiguous range of logical tiles, ordered in groups of
-//    8 row-tiles to share A and B panels in that XCD's L2, dealt round-robin
-//    to its workgroups.
+//    8 row-tiles (2 when a row of A holds 8 KB or more) to share A and B
+//    panels in that XCD's L2, dealt round-robin to its workgroups.
 //  * Ragged M / N: operand loads go through buffer resources bounded at the
 //    tile's last valid row (the hardware returns zero beyond it), stores are
 //    masked.  K must be a multiple of 64.
@@ -146,7 +146,11 @@ constexpr int BM = 256, BN = 256, BK = 64, NTHR = 512;
 constexpr int BK8 = 128;                    // fp8 operands: k-values per 128-byte LDS row
 constexpr int NE = 5;                       // entries in the operand ring
 constexpr int ENT = BM * BK * 2;            // 32 KB: one operand slab (256 rows x 128 B)
-constexpr int GROUP_M = 8;
+// Row-tiles per tile group (the tiles of a group share A and B panels in one
+// XCD's L2).  Measured on the isolated shapes at M = 206,400: K = 1024 runs best
+// at 8 (MLP-up 1% slower at 2), K = 4096 (MLP-down) at 2 (3.5% faster than 8).
+// Which CU computes which tile never changes a tile's arithmetic.
+constexpr int GROUP_M = 8, GROUP_M_LONG_K = 2;
 
 
 struct TileCoord {
@@ -194,8 +198,9 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
   const int KT = K / KS;
 
   // This workgroup's tiles.  The dispatcher hands workgroup b to XCD b % 8; XCD x
-  // owns a contiguous range of logical tiles (groups of 8 row-tiles sharing A and
+  // owns a contiguous range of logical tiles (groups of gm row-tiles sharing A and
   // B panels in that XCD's L2), dealt round-robin to its workgroups.
+  const int gm = K * ES >= 8192 ? GROUP_M_LONG_K : GROUP_M;
   const int G = gridDim.x, xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int sx = (G >> 3) + (xcd < (G & 7) ? 1 : 0);
   const int tbase = tiles >> 3, trem = tiles & 7;
@@ -205,10 +210,10 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
     const int idx = slot + i * sx;
     if (idx < tcnt) {
       const int L = tlo + idx;
-      const int per_group = GROUP_M * tiles_n;
+      const int per_group = gm * tiles_n;
       const int g = L / per_group;
-      const int first_m = g * GROUP_M;
-      const int gsize = min(tiles_m - first_m, GROUP_M);
+      const int first_m = g * gm;
+      const int gsize = min(tiles_m - first_m, gm);
       const int in = L - g * per_group;
       t.m0 = (first_m + in % gsize) * BM;
       t.n0 = (in / gsize) * BN;
