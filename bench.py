@@ -49,8 +49,8 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
 # as null once those change.
 GEMM_COUNTERS = {
-    "sources_sha256": "bd1c43f3eef799f9b21ca0b12475a3ea7a80baa68b4a6075c36f67222d7f2e15",
-    "bytes_per_launch": 3688349990,
+    "sources_sha256": "91d45b8f451be778e69c7e54d72e8c0c361b28915f0d669d22bb78076405f8dc",
+    "bytes_per_launch": 3446157282,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 
