@@ -44,8 +44,12 @@
 //    8 row-tiles (2 when a row of A holds 8 KB or more) to share A and B
 //    panels in that XCD's L2, dealt round-robin to its workgroups.
 //  * Ragged M / N: operand loads go through buffer resources bounded at the
-//    tile's last valid row (the hardware returns zero beyond it), stores are
-//    masked.  K must be a multiple of 64.
+//    tile's last valid row (the hardware returns zero beyond it).  Results, and
+//    the residual rows the residual kind adds, go through buffer resources
+//    bounded at row M as well (row-remapped outputs use masked stores).  With
+//    only buffer operations in flight the compiler counts each wait on a
+//    residual load exactly instead of draining every load.  K must be a
+//    multiple of 64.
 //  * Results leave through the ring entry that the tile's last slab frees
 //    and that the next load into it waits for (4 KB a wave, 32 rows at a
 //    time) as full 128-byte row pieces, stored non-temporally (this kernel
@@ -85,6 +89,18 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 __device__ __forceinline__ void lds_write_b64(uint8_t* p, uint2 v) {
   const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
   asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void lds_write_b128(uint8_t* p, u32x4 v) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
+// A value every lane holds alike, moved to scalar registers: buffer resources built
+// from it then stay scalar instead of being taken apart lane by lane.
+__device__ __forceinline__ uint64_t uniform_u64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
 }
 
 // ------------------------------------------------------------------ epilogue
@@ -168,7 +184,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t slab_rsrc(const void* base, in
       (short)0, (int)bytes, 0x00020000);
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8_t __attribute__((ext_vector_type(8)));
 
 // AFF (affine rows): out = s_m ((A Bt^T)[m, n] - shift_m col_n) + w_scale bias_n with
@@ -506,12 +521,15 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
     const int ldc = to_c0 ? epi.ld0 : epi.ld1;
     const int cshift = to_c0 ? 0 : epi.split;
     if ((to_c0 || to_c1) && T.n0 + BN <= N && (ldc & 7) == 0 && (cshift & 7) == 0 &&
-        epi.rows.group >= 8 && ((uintptr_t)cbase & 15) == 0) {
+        (KIND == kEpiResidual ? epi.rows.group > M : epi.rows.group >= 8) &&
+        ((uintptr_t)cbase & 15) == 0) {
       // Each wave stages its 128 x 64 result 32 rows at a time in its own 4 KB of
       // the free ring entry (row r: 128 bytes, 16-byte chunk c at c ^ ((r >> 1) & 7)),
       // then writes whole 128-byte row pieces (8 rows per store instruction).
       uint8_t* const ep = lds + stage_ep * ENT + wave * 4096;
-      bf16* const cwave = cbase + (T.n0 + wn * 64 - cshift);
+      bf16* const cwave =
+          reinterpret_cast<bf16*>(uniform_u64(reinterpret_cast<uintptr_t>(cbase + (T.n0 + wn * 64 - cshift))));
+      const int ldcu = __builtin_amdgcn_readfirstlane(ldc);
       const int row_base = T.m0 + wm * 128;
       const bool plain_rows = epi.rows.group > M;
       // destination row of local row 8 t + lane / 8 of each 32-row block, walked in
@@ -530,17 +548,27 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
         return q;
       };
       const int c16r = lane & 7;
+      // Plain rows: one buffer resource per 8-row piece, its record count ending at
+      // row M (rows past it read zero and are not written), and one per-lane byte
+      // offset (row lane / 8, 16-byte chunk lane % 8).  The residual kind reads and
+      // writes only through these, so every wait on its loads is counted exactly.
+      const int vro = ((lane >> 3) * ldcu + c16r * 8) * 2;
+      auto piece_rsrc = [&](int i, int t) {
+        const int r0 = row_base + 32 * i + 8 * t;
+        // rows of this piece inside M, clamped to 0..8 on the scalar unit (a clamp
+        // written in C becomes a vector med3 and the resource a per-lane loop)
+        int nr;
+        asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, 8" : "=s"(nr) : "s"(M - r0) : "scc");
+        bf16* const base = cwave + ((long long)epi.rows.offset + r0) * ldcu;
+        return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nr * ldcu * 2, 0x00020000);
+      };
       if constexpr (KIND == kEpiResidual) {
         // the residual rows, loaded two blocks ahead (16 bytes a lane, 8 rows per load)
         u32x4 res[3][4];
         auto load_res = [&](int i, u32x4 (&r)[4]) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int m = row_base + i * 32 + 8 * t + (lane >> 3);
-            const long long row = plain_rows ? (long long)epi.rows.offset + m : epi.rows(m);
-            r[t] = u32x4{0u, 0u, 0u, 0u};
-            if (m < M) r[t] = *reinterpret_cast<const u32x4*>(cwave + row * ldc + c16r * 8);
-          }
+          for (int t = 0; t < 4; ++t)
+            r[t] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(piece_rsrc(i, t), vro, 0, 0));
         };
         load_res(0, res[0]);
         load_res(1, res[1]);
@@ -551,7 +579,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int rr = 8 * t + (lane >> 3);
-            *reinterpret_cast<u32x4*>(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4)) = res[i % 3][t];
+            lds_write_b128(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4), res[i % 3][t]);
           }
           // add the accumulators in fp32 and round once, in place
 #pragma unroll
@@ -566,7 +594,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
                                 __uint_as_float(u.x & 0xffff0000u) + acc[i][j][4 * q + 1]);
               o.y = pack_bf16x2(__uint_as_float(u.y << 16) + acc[i][j][4 * q + 2],
                                 __uint_as_float(u.y & 0xffff0000u) + acc[i][j][4 * q + 3]);
-              *slotp = o;
+              lds_write_b64(reinterpret_cast<uint8_t*>(slotp), o);
             }
           u32x4 d[4];
 #pragma unroll
@@ -575,11 +603,7 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
             d[t] = *reinterpret_cast<const u32x4*>(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4));
           }
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int m = row_base + i * 32 + 8 * t + (lane >> 3);
-            bf16* const dst = plain_rows ? cwave + ((long long)epi.rows.offset + m) * ldc : next_row();
-            if (m < M) __builtin_nontemporal_store(d[t], reinterpret_cast<u32x4*>(dst + c16r * 8));
-          }
+          for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(d[t], piece_rsrc(i, t), vro, 0, 2);
           F;
         }
       } else {
@@ -611,11 +635,16 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
             const int rr = 8 * t + (lane >> 3);
             d[t] = *reinterpret_cast<const u32x4*>(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4));
           }
+          if (plain_rows) {
 #pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            const int m = row_base + i * 32 + 8 * t + (lane >> 3);
-            bf16* const dst = plain_rows ? cwave + ((long long)epi.rows.offset + m) * ldc : next_row();
-            if (m < M) __builtin_nontemporal_store(d[t], reinterpret_cast<u32x4*>(dst + c16r * 8));
+            for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(d[t], piece_rsrc(i, t), vro, 0, 2);
+          } else {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+              const int m = row_base + i * 32 + 8 * t + (lane >> 3);
+              bf16* const dst = next_row();
+              if (m < M) __builtin_nontemporal_store(d[t], reinterpret_cast<u32x4*>(dst + c16r * 8));
+            }
           }
           F;
         }
