@@ -25,8 +25,11 @@
 //    (ds_read_b64_tr_b16): lane 16 g + 4 r + c reads 4 dh-values of key r,
 //    lane 16 g + i receives 4 keys of dh-row i.
 //  * HBM traffic per (candidate, head) is one read of Q, K, V and one write of
-//    O: at the V-JEPA2-AC shape the bound is HBM bandwidth plus the
-//    per-score exp2.
+//    O.  At the V-JEPA2-AC shape that traffic alone would take about 0.2 ms
+//    per launch; the kernel takes about twice that, with neither the vector
+//    ALUs nor the matrix cores saturated: its dependency chains (scores ->
+//    max -> exp2 -> P V) at four waves per SIMD, and the K/V staging of each
+//    workgroup, set the pace.  exp2 issues at the rate of an fma here.
 //
 // Several frame blocks (KV cache, horizon > 1): the same 512-thread structure
 // with the blocks streamed through LDS one at a time and, per query tile, the
