@@ -45,7 +45,10 @@ def gpu_rollout(name, actions):
     return to_np(zp)
 
 
-@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("oddk", 9), ("small_fp8", 12)])
+# small with n = 3 and 5 (M = 198, 330 rows): the last rows of each GEMM fill an 8-row piece only
+# partly (6 and 2 rows), in the residual kind's buffer-bounded epilogue as well
+@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("small", 3), ("small", 5),
+                                    ("oddk", 9), ("small_fp8", 12)])
 def test_rollout_matches_oracle(gpu_lib, name, n):
     from cem_jepa_predictor_amd import inputs
 
