@@ -282,7 +282,10 @@ def _problems(name, batch):
     return [np.stack(v) for v in (zo, zg, st, mu, sg)]
 
 
-@pytest.mark.parametrize("name,batch,use_graph", [("tiny", 3, True), ("small", 2, True), ("tiny", 2, False)])
+# sweep_400 x 2: two V-JEPA2-AC-shaped problems of 400 candidates in one 800-candidate batch
+# (M = 206,400 rows), as the benchmark's fleet-batching rows run it
+@pytest.mark.parametrize("name,batch,use_graph", [("tiny", 3, True), ("small", 2, True), ("tiny", 2, False),
+                                                  ("sweep_400", 2, True)])
 def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
     """Fleet batching (page section 06 C): a batched plan of several problems in one
     predictor batch gives each problem exactly its own cem_plan result (plan id
@@ -335,7 +338,8 @@ def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
     # the problems really differ
     assert not np.array_equal(tb["e"][:, :N], tb["e"][:, N:2 * N])
     # and every problem's slice follows the oracle round by round on its own inputs,
-    # Gaussian and plan id (all candidates for tiny, 6 per round for small)
+    # Gaussian and plan id (all candidates for tiny, 6 per round for small, 2 per round at
+    # the V-JEPA2-AC shape)
     for b in range(batch):
         out_b = {"x": tb["x"][:, b * N:(b + 1) * N], "energy": tb["e"][:, b * N:(b + 1) * N],
                  "elites": tb["el"][:, b], "mu": tb["mu"][:, b], "sigma": tb["sg"][:, b],
@@ -344,7 +348,8 @@ def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
         if name == "tiny":
             rows = lambda r, n: np.arange(n)  # noqa: E731
         else:
-            rows = lambda r, n, b=b: np.random.default_rng(10 * b + r).choice(n, 6, replace=False)  # noqa: E731
+            per_round = 6 if name == "small" else 2
+            rows = lambda r, n, b=b, k=per_round: np.random.default_rng(10 * b + r).choice(n, k, replace=False)  # noqa: E731
         worst = _lockstep(name, out_b, rows, mu_init=mu[b], sigma_init=sg[b], plan_id=4 + b,
                           problem=(zo[b], zg[b], st[b]))
         log(f"  problem {b}: lockstep with the oracle, worst energy rel err {worst:.3e}")
