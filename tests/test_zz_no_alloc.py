@@ -37,6 +37,7 @@ def _plan(name, *, noalloc, n, k, rounds, horizon, plan_id=0, seed=None):
 @pytest.mark.parametrize("name,shapes", [
     ("small", [(256, 32, 3, 3), (64, 8, 2, 2)]),   # bf16, horizon 3 then a smaller plan
     ("tiny", [(64, 8, 3, 2), (17, 5, 1, 1)]),      # fp32
+    ("vjepa2ac", [(800, 80, 2, 1), (200, 20, 1, 1)]),   # the measured shape, then a smaller plan
 ])
 def test_noalloc_plan_equals_cem_plan(gpu_lib, name, shapes):
     for i, (n, k, r, h) in enumerate(shapes):
