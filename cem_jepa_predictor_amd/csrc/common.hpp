@@ -65,6 +65,10 @@ struct Epilogue {
   int gelu;            // 1: GELU after the bias
   int residual;        // 1: add the existing output value
   RowMap rows;
+  // residual kind only, nullable: per-row statistics of the rounded output, one
+  // (mean, sum of squared deviations) pair per 64-column piece, piece p of row m
+  // at stats[2 (p M + m)]
+  float* stats = nullptr;
 };
 
 enum class Act { None, Gelu };

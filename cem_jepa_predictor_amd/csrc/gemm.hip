@@ -90,6 +90,8 @@ __device__ __forceinline__ void lds_write_b64(uint8_t* p, uint2 v) {
   const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
   asm volatile("ds_write_b64 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void lds_write_b128(uint8_t* p, u32x4 v) {
   const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
@@ -563,8 +565,15 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
         return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, nr * ldcu * 2, 0x00020000);
       };
       if constexpr (KIND == kEpiResidual) {
+        // output row statistics: pieces of 64 columns, one per wave, written as
+        // (mean, sum of squared deviations) for rows below M
+        const bool want_stats = epi.stats != nullptr;
+        const __amdgpu_buffer_rsrc_t rstat = __builtin_amdgcn_make_buffer_rsrc(
+            want_stats ? epi.stats + 2LL * ((T.n0 >> 6) + wn) * M : nullptr, (short)0, want_stats ? M * 8 : 0,
+            0x00020000);
         // the residual rows, loaded two blocks ahead (16 bytes a lane, 8 rows per load)
-        u32x4 res[3][4];
+        // into the registers the block before them has just left for the staging slots
+        u32x4 res[2][4];
         auto load_res = [&](int i, u32x4 (&r)[4]) {
 #pragma unroll
           for (int t = 0; t < 4; ++t)
@@ -574,13 +583,13 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
         load_res(1, res[1]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if (i + 2 < 4) load_res(i + 2, res[(i + 2) % 3]);
           // residual rows into the staging slots
 #pragma unroll
           for (int t = 0; t < 4; ++t) {
             const int rr = 8 * t + (lane >> 3);
-            lds_write_b128(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4), res[i % 3][t]);
+            lds_write_b128(ep + rr * 128 + ((c16r ^ ((rr >> 1) & 7)) << 4), res[i % 2][t]);
           }
+          if (i + 2 < 4) load_res(i + 2, res[i % 2]);
           // add the accumulators in fp32 and round once, in place
 #pragma unroll
           for (int j = 0; j < 2; ++j)
@@ -604,6 +613,32 @@ __global__ __launch_bounds__(NTHR) void gemm_bf16_kernel(const void* __restrict_
           }
 #pragma unroll
           for (int t = 0; t < 4; ++t) __builtin_amdgcn_raw_buffer_store_b128(d[t], piece_rsrc(i, t), vro, 0, 2);
+          F;
+          if (want_stats) {
+            // row fr's 64 columns of this wave: 32 in this lane (read back from its
+            // staging slots), 32 in lane fr + 32.  One pass in fp32 (bf16 pair products
+            // are exact): the squared deviations are sum(v^2) - sum(v)^2 / 64, relative
+            // error about 2^-17 (1 + mean^2 / variance) of the piece
+            float s = 0.f, s2 = 0.f;
+            const bf16x2_t ones = __builtin_bit_cast(bf16x2_t, 0x3f803f80u);
+#pragma unroll
+            for (int c16 = 0; c16 < 8; ++c16) {
+              const uint2 o = *reinterpret_cast<const uint2*>(ep + fr * 128 + ((c16 ^ ((fr >> 1) & 7)) << 4) + fk * 8);
+              const bf16x2_t px = __builtin_bit_cast(bf16x2_t, o.x), py = __builtin_bit_cast(bf16x2_t, o.y);
+              s = __builtin_amdgcn_fdot2_f32_bf16(px, ones, s, false);
+              s = __builtin_amdgcn_fdot2_f32_bf16(py, ones, s, false);
+              s2 = __builtin_amdgcn_fdot2_f32_bf16(px, px, s2, false);
+              s2 = __builtin_amdgcn_fdot2_f32_bf16(py, py, s2, false);
+            }
+            const auto sp = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+            const auto qp = __builtin_amdgcn_permlane32_swap(__float_as_uint(s2), __float_as_uint(s2), false, false);
+            const float sum = __uint_as_float(sp[0]) + __uint_as_float(sp[1]);
+            const float mean = sum * (1.0f / 64.0f);
+            const float m2 = fmaxf(fmaf(-sum, mean, __uint_as_float(qp[0]) + __uint_as_float(qp[1])), 0.f);
+            // lanes 0..31 write rows row_base + 32 i + fr; rows at or past M are out of range
+            const int off = fk == 0 ? (row_base + 32 * i + fr) * 8 : 0x7ffffff0;
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(mean), __float_as_uint(m2)}, rstat, off, 0, 0);
+          }
           F;
         }
       } else {
@@ -763,6 +798,10 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
                             const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K <= 0 || K % BK != 0) return hipErrorInvalidValue;
+  // row statistics come from the staged epilogue, which every tile must take
+  if (epi.stats && !(epi.residual && N % BN == 0 && epi.split >= N && (epi.ld0 & 7) == 0 &&
+                     epi.rows.group > M && ((uintptr_t)epi.c0 & 15) == 0))
+    return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = cu_count(&cus);
   if (ce != hipSuccess) return ce;
@@ -784,7 +823,7 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
 hipError_t launch_gemm_bf16_rows(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N, int K,
                                  const float* row_vals, const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (K <= 0 || K % BK != 0 || !row_vals || epi.residual) return hipErrorInvalidValue;
+  if (K <= 0 || K % BK != 0 || !row_vals || epi.residual || epi.stats) return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = cu_count(&cus);
   if (ce != hipSuccess) return ce;
@@ -801,7 +840,7 @@ hipError_t launch_gemm_fp8(const uint8_t* A, int lda, const uint8_t* Bt, int ldb
                            const float* row_scale, float w_scale, const Epilogue& epi,
                            hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  if (K <= 0 || K % BK8 != 0 || !row_scale || epi.residual) return hipErrorInvalidValue;
+  if (K <= 0 || K % BK8 != 0 || !row_scale || epi.residual || epi.stats) return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = cu_count(&cus);
   if (ce != hipSuccess) return ce;
@@ -817,6 +856,7 @@ hipError_t launch_gemm_fp8(const uint8_t* A, int lda, const uint8_t* Bt, int ldb
 hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N, int K,
                            const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
+  if (epi.stats) return hipErrorInvalidValue;
   dim3 grid((N + FBN - 1) / FBN, (M + FBM - 1) / FBM);
   switch (epi_kind(epi)) {
     case kEpiGelu:

@@ -51,13 +51,19 @@ hipError_t launch_layernorm_fp8(const bf16* x, int rows, int d, RowMap in_rows, 
 // 1 / sqrt(biased variance + eps), fp32, the LayerNorm kernel's arithmetic.
 hipError_t launch_row_stats(const bf16* x, int rows, int d, float eps, float* mean, float* rstd,
                             hipStream_t stream);
+// The same statistics of rows [rows, d] (d % 64 == 0) from the per-64-column partial
+// statistics a residual GEMM wrote for them (Epilogue::stats).
+hipError_t launch_row_stats_combine(const float* parts, int rows, int d, float eps, float* mean,
+                                    float* rstd, hipStream_t stream);
 // The same per-row quantization of fp32 rows [rows, cols] (cols % 8 == 0).
 hipError_t launch_quantize_rows_fp8(const float* x, int rows, int cols, uint8_t* y8,
                                     float* row_scale, hipStream_t stream);
 
 // --- gemm.hip ----------------------------------------------------------------
 // out = epilogue(A[M, K] @ Bt[N, K]^T); N % 4 == 0; bf16 (MFMA): K % 64 == 0
-// (hipErrorInvalidValue otherwise); fp32: K % 16 == 0.
+// (hipErrorInvalidValue otherwise); fp32: K % 16 == 0.  epi.stats (bf16 residual
+// kind only) also needs N % 256 == 0, one output (split >= N) with ld0 % 8 == 0 and
+// a 16-byte aligned c0, and identity rows; the other launchers reject it.
 hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N,
                             int K, const Epilogue& epi, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N,

@@ -264,6 +264,32 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const bf16* __restrict__
   }
 }
 
+// Row statistics from partial statistics of 64-column pieces, written by the
+// residual GEMM that produced the rows: piece p of row r holds the mean and the
+// sum of squared deviations of its 64 values at parts[2 (p rows + r)].  Exact
+// decomposition of the same two quantities over the whole row: the mean is the
+// average of the piece means, and the sum of squared deviations is the sum over
+// pieces of (piece sum + 64 (piece mean - mean)^2).  One thread per row; reads
+// 8 bytes per piece and row (coalesced across the rows of a piece).
+__global__ __launch_bounds__(256) void row_stats_combine_kernel(const float2* __restrict__ parts,
+                                                                int pieces, int rows, float eps,
+                                                                float* __restrict__ mean_out,
+                                                                float* __restrict__ rstd_out) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= rows) return;
+  float sm = 0.f;
+  for (int p = 0; p < pieces; ++p) sm += parts[(long long)p * rows + r].x;
+  const float mean = sm / (float)pieces;
+  float q = 0.f;
+  for (int p = 0; p < pieces; ++p) {
+    const float2 v = parts[(long long)p * rows + r];
+    const float dm = v.x - mean;
+    q += fmaf(64.0f * dm, dm, v.y);
+  }
+  mean_out[r] = mean;
+  rstd_out[r] = rsqrtf(q / (64.0f * (float)pieces) + eps);
+}
+
 template <int NCH, typename T>
 hipError_t run(const T* x, int rows, RowMap in_rows, const float* g, const float* b, float eps,
                T* y, hipStream_t stream) {
@@ -349,6 +375,15 @@ hipError_t launch_row_stats(const bf16* x, int rows, int d, float eps, float* me
     default: return hipErrorInvalidValue;
   }
 #undef CEM_STATS
+  return hipGetLastError();
+}
+
+hipError_t launch_row_stats_combine(const float* parts, int rows, int d, float eps, float* mean,
+                                    float* rstd, hipStream_t stream) {
+  if (rows <= 0) return hipSuccess;
+  if (d <= 0 || d % 64 != 0 || !parts) return hipErrorInvalidValue;
+  row_stats_combine_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(reinterpret_cast<const float2*>(parts),
+                                                                   d / 64, rows, eps, mean, rstd);
   return hipGetLastError();
 }
 

@@ -363,6 +363,8 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   const size_t o_f0 = al.take(P * D * es), o_zobs = al.take(P * E * es);
   const size_t o_h8 = al.take(m->fp8 ? rows * D : 0), o_hs = al.take(m->fp8 ? rows * 4 : 0);
   const size_t o_stats = al.take(fold * 2 * rows * 4);
+  const size_t parts = (fold && D % 256 == 0) ? 1 : 0;   // residual GEMMs write LN statistics
+  const size_t o_parts = al.take(parts * (D / 64) * rows * 8);
   e = hipMalloc(&m->arena, al.off);
   if (e != hipSuccess) return fail(hip_status(e, "hipMalloc(workspace)"));
   uint8_t* ab = static_cast<uint8_t*>(m->arena);
@@ -370,6 +372,7 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   m->zhat = ab + o_zhat; m->f0 = ab + o_f0; m->zobs_t = ab + o_zobs;
   if (m->fp8) { m->h8 = ab + o_h8; m->hs = reinterpret_cast<float*>(ab + o_hs); }
   if (m->ln_fold) m->ln_stats = reinterpret_cast<float*>(ab + o_stats);
+  if (parts) m->ln_parts = reinterpret_cast<float*>(ab + o_parts);
 
   e = select_init();
   if (e != hipSuccess) return fail(hip_status(e, "select_init"));
@@ -442,12 +445,15 @@ hipError_t gemm8(cem_model* m, const uint8_t* A, int lda, const void* Bt, int ld
 }
 
 // bf16 GEMM over M raw residual rows with the LayerNorm before it folded in: row
-// statistics of those rows, then the GEMM with rstd / mean row terms and the folded
-// bias / column-sum terms (e.bias, 2 N floats)
+// statistics of those rows (combined from the partial statistics of the residual
+// GEMM that wrote them when `from_parts`, else read from the rows), then the GEMM
+// with rstd / mean row terms and the folded bias / column-sum terms (e.bias, 2 N floats)
 hipError_t gemm_ln(cem_model* m, const void* A, int lda, const void* Bt, int ldb, int M, int N, int K,
-                   const Epilogue& e, hipStream_t st) {
-  hipError_t r = launch_row_stats(static_cast<const bf16*>(A), M, K, m->desc.ln_eps,
-                                  m->ln_stats + M, m->ln_stats, st);
+                   const Epilogue& e, bool from_parts, hipStream_t st) {
+  hipError_t r = from_parts ? launch_row_stats_combine(m->ln_parts, M, K, m->desc.ln_eps, m->ln_stats + M,
+                                                       m->ln_stats, st)
+                            : launch_row_stats(static_cast<const bf16*>(A), M, K, m->desc.ln_eps,
+                                               m->ln_stats + M, m->ln_stats, st);
   if (r != hipSuccess) return r;
   r = timer_start(m, st, 2.0 * M * (double)N * K);
   if (r != hipSuccess) return r;
@@ -458,10 +464,10 @@ hipError_t gemm_ln(cem_model* m, const void* A, int lda, const void* Bt, int ldb
 }
 
 Epilogue epi(const float* bias, void* c0, int ld0, int split, void* c1 = nullptr, int ld1 = 0,
-             int gelu = 0, int residual = 0, RowMap rows = RowMap::identity()) {
+             int gelu = 0, int residual = 0, RowMap rows = RowMap::identity(), float* stats = nullptr) {
   Epilogue e;
   e.bias = bias; e.c0 = c0; e.c1 = c1; e.ld0 = ld0; e.ld1 = ld1; e.split = split;
-  e.gelu = gelu; e.residual = residual; e.rows = rows;
+  e.gelu = gelu; e.residual = residual; e.rows = rows; e.stats = stats;
   return e;
 }
 
@@ -513,8 +519,9 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
         RUN(gemm8(m, m->h8, D, w.w_qkv_t, D, rows, 3 * D, D, m->hs, w.ws_qkv,
                   epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
       } else if (m->ln_fold) {
+        // layer 0's input rows come from the token embedding, the others' from a residual GEMM
         RUN(gemm_ln(m, m->x, D, w.w_qkv_t, D, rows, 3 * D, D,
-                    epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
+                    epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), l > 0 && m->ln_parts, st));
       } else {
         RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
                                 w.ln1_b, d.ln_eps, static_cast<T*>(m->h), st));
@@ -528,20 +535,25 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
       a.n = n; a.heads = d.heads; a.dh = D / d.heads; a.d = D; a.B = B; a.nblk = t + 1;
       a.scale = 1.0f / std::sqrt((float)a.dh);
       RUN(m->bf16 ? launch_attention_bf16(a, st) : launch_attention_f32(a, st));
-      RUN(gemm(m, m->h, D, w.w_o_t, D, rows, D, D, epi(w.b_o, m->x, D, D, nullptr, 0, 0, 1), st));
+      RUN(gemm(m, m->h, D, w.w_o_t, D, rows, D, D,
+               epi(w.b_o, m->x, D, D, nullptr, 0, 0, 1, RowMap::identity(), m->ln_parts), st));
       if (m->fp8) {
         RUN(launch_layernorm_fp8(static_cast<const bf16*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
                                  w.ln2_b, d.ln_eps, m->h8, m->hs, st));
         RUN(gemm8(m, m->h8, D, w.w_1_t, D, rows, F, D, m->hs, w.ws_1,
                   epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
       } else if (m->ln_fold) {
-        RUN(gemm_ln(m, m->x, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
+        RUN(gemm_ln(m, m->x, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0),
+                    m->ln_parts != nullptr, st));
       } else {
         RUN(launch_layernorm<T>(static_cast<const T*>(m->x), rows, D, RowMap::identity(), w.ln2_g,
                                 w.ln2_b, d.ln_eps, static_cast<T*>(m->h), st));
         RUN(gemm(m, m->h, D, w.w_1_t, D, rows, F, D, epi(w.b_1, m->u, F, F, nullptr, 0, 1, 0), st));
       }
-      RUN(gemm(m, m->u, F, w.w_2_t, F, rows, D, F, epi(w.b_2, m->x, D, D, nullptr, 0, 0, 1), st));
+      // the last layer's rows go to the final LayerNorm, which computes its own statistics
+      RUN(gemm(m, m->u, F, w.w_2_t, F, rows, D, F,
+               epi(w.b_2, m->x, D, D, nullptr, 0, 0, 1, RowMap::identity(),
+                   l + 1 < d.layers ? m->ln_parts : nullptr), st));
     }
     // final LayerNorm of the patch rows, then the out-projection to the encoder width
     RUN(launch_layernorm<T>(static_cast<const T*>(m->x), n * P, D, RowMap{P, B, 2}, m->lnf_g,

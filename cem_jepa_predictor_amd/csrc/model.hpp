@@ -91,6 +91,8 @@ struct cem_model {
   uint8_t* h8 = nullptr;   // fp8 models: e4m3 LayerNorm output [rows, d]
   float* hs = nullptr;     // and its row scales [rows]
   float* ln_stats = nullptr;   // LayerNorm-folded models: [rstd | mean] of the rows of one call
+  float* ln_parts = nullptr;   // and, for d % 256 == 0, the residual GEMMs' per-64-column
+                               // (mean, squared deviations) of the rows they write
 
   cem::PlanState plan;
   hipStream_t cap_stream = nullptr;

@@ -476,14 +476,16 @@ def test_fp8_rollout_is_the_fp8_method(gpu_lib, name):
     assert d0 >= 0.8
 
 
-@pytest.mark.parametrize("name,n", [("small", 64), ("vjepa2ac", 16)])
-def test_energy_ranking_with_reachable_goal(gpu_lib, name, n):
+@pytest.mark.parametrize("name,n,draws", [("small", 64, 4), ("vjepa2ac", 16, 1)])
+def test_energy_ranking_with_reachable_goal(gpu_lib, name, n, draws):
     """Energy parity as a ranking (page section 05: the bf16 planner's energies track the
     fp32 reference, Pearson r 0.9999).  With the workload's random goal the candidates'
     energies differ by little more than bf16 storage of the residual stream moves them
     (any bf16 implementation; logged).  With a reachable goal -- the oracle's predicted
     frame for a known action sequence -- candidates differ by how far their actions are
-    from it, and the GPU's energies must rank them as the oracle does."""
+    from it, and the GPU's energies must rank them as the oracle does.  On small, r is
+    pooled over `draws` action draws of n candidates: the r of one 64-candidate draw moves
+    by about 3e-4 with the bf16 rounding pattern alone."""
     from cem_jepa_predictor_amd import inputs
 
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
@@ -491,9 +493,12 @@ def test_energy_ranking_with_reachable_goal(gpu_lib, name, n):
     pred = oracle_predictor(name)
     a_star = inputs.make_actions(1, H, seed=99) * np.float32(0.6)
     goal = pred.rollout_cached(a_star, z_obs, s0)[0].astype(np.float32)
-    actions = inputs.make_actions(n, H, seed=51)
-    got = gpu_rollout(name, actions)
-    want = pred.rollout_cached(actions, z_obs, s0)
+    got, want = [], []
+    for k in range(draws):
+        actions = inputs.make_actions(n, H, seed=51 + k)
+        got.append(gpu_rollout(name, actions))
+        want.append(pred.rollout_cached(actions, z_obs, s0))
+    got, want = np.concatenate(got), np.concatenate(want)
     stats = {}
     for label, g in (("random goal", z_goal), ("reachable goal", goal)):
         e_got, e_want = o_energy.energy_l1(got, g), o_energy.energy_l1(want, g)
@@ -501,8 +506,8 @@ def test_energy_ranking_with_reachable_goal(gpu_lib, name, n):
         d = e_got - e_want
         spread, err = float(np.std(e_want)), float(np.std(d))
         stats[label] = r
-        log(f"  {name} {label}: mean energy {e_want.mean():.4e}, Pearson r {r:.6f}, spread {spread:.3e}, "
-            f"candidate-specific rms err {err:.3e} (ratio {spread / max(err, 1e-30):.1f}), "
+        log(f"  {name} {label} ({draws} x {n} candidates): mean energy {e_want.mean():.4e}, Pearson r {r:.6f}, "
+            f"spread {spread:.3e}, candidate-specific rms err {err:.3e} (ratio {spread / max(err, 1e-30):.1f}), "
             f"common offset {d.mean():.3e}")
     # bf16 storage of the residual stream alone, emulated on the oracle, gives r of
     # 0.9993 on small; at 24 layers it is a larger share of the smaller effect of an
