@@ -49,8 +49,8 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
 # as null once those change.
 GEMM_COUNTERS = {
-    "sources_sha256": "dc79eda98a718a576b0a0dbc3bcc24fcec33e08ffb72c16e4ee92b8fed2ae6b0",
-    "bytes_per_launch": 3423720328,
+    "sources_sha256": "5e982de44d976e43a3c7e4a624fa0e58688a67fcd0c251ebc761c138a99b9bdf",
+    "bytes_per_launch": 3478995885,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 

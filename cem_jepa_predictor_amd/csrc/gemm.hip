@@ -73,7 +73,11 @@
 // Epilogue (fp32): + bias (already in the accumulators), optional GELU,
 // optional residual add (the output already holds the residual stream),
 // optional column split into two destinations (q -> Q buffer, k|v -> KV
-// cache), optional output-row remap.
+// cache), optional output-row remap.  The residual kind can also write the
+// statistics the next LayerNorm needs (its input is this output): for every
+// 64-column piece of every row, the mean and sum of squared deviations of the
+// rounded values, read back from the staging slots after the block's stores
+// have been issued.
 #include "kernels.hpp"
 
 namespace cem {

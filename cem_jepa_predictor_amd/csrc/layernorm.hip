@@ -269,25 +269,43 @@ __global__ __launch_bounds__(256) void row_stats_kernel(const bf16* __restrict__
 // sum of squared deviations of its 64 values at parts[2 (p rows + r)].  Exact
 // decomposition of the same two quantities over the whole row: the mean is the
 // average of the piece means, and the sum of squared deviations is the sum over
-// pieces of (piece sum + 64 (piece mean - mean)^2).  One thread per row; reads
-// 8 bytes per piece and row (coalesced across the rows of a piece).
+// pieces of (piece sum + 64 (piece mean - mean)^2).  One thread per row, all P
+// pieces loaded at once (8 bytes per piece and row, coalesced across the rows of
+// a piece); P = 0: the piece count comes at run time and the pieces are read twice.
+template <int P>
 __global__ __launch_bounds__(256) void row_stats_combine_kernel(const float2* __restrict__ parts,
                                                                 int pieces, int rows, float eps,
                                                                 float* __restrict__ mean_out,
                                                                 float* __restrict__ rstd_out) {
   const int r = blockIdx.x * 256 + threadIdx.x;
   if (r >= rows) return;
-  float sm = 0.f;
-  for (int p = 0; p < pieces; ++p) sm += parts[(long long)p * rows + r].x;
-  const float mean = sm / (float)pieces;
-  float q = 0.f;
-  for (int p = 0; p < pieces; ++p) {
-    const float2 v = parts[(long long)p * rows + r];
-    const float dm = v.x - mean;
-    q += fmaf(64.0f * dm, dm, v.y);
+  const int np = P > 0 ? P : pieces;
+  float mean, q = 0.f;
+  if constexpr (P > 0) {
+    float2 v[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) v[p] = parts[(long long)p * rows + r];
+    float sm = 0.f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) sm += v[p].x;
+    mean = sm / (float)P;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const float dm = v[p].x - mean;
+      q += fmaf(64.0f * dm, dm, v[p].y);
+    }
+  } else {
+    float sm = 0.f;
+    for (int p = 0; p < np; ++p) sm += parts[(long long)p * rows + r].x;
+    mean = sm / (float)np;
+    for (int p = 0; p < np; ++p) {
+      const float2 v = parts[(long long)p * rows + r];
+      const float dm = v.x - mean;
+      q += fmaf(64.0f * dm, dm, v.y);
+    }
   }
   mean_out[r] = mean;
-  rstd_out[r] = rsqrtf(q / (64.0f * (float)pieces) + eps);
+  rstd_out[r] = rsqrtf(q / (64.0f * (float)np) + eps);
 }
 
 template <int NCH, typename T>
@@ -382,8 +400,14 @@ hipError_t launch_row_stats_combine(const float* parts, int rows, int d, float e
                                     float* rstd, hipStream_t stream) {
   if (rows <= 0) return hipSuccess;
   if (d <= 0 || d % 64 != 0 || !parts) return hipErrorInvalidValue;
-  row_stats_combine_kernel<<<(rows + 255) / 256, 256, 0, stream>>>(reinterpret_cast<const float2*>(parts),
-                                                                   d / 64, rows, eps, mean, rstd);
+  const float2* pp = reinterpret_cast<const float2*>(parts);
+  const int grid = (rows + 255) / 256;
+  switch (d / 64) {
+    case 8: row_stats_combine_kernel<8><<<grid, 256, 0, stream>>>(pp, 8, rows, eps, mean, rstd); break;
+    case 16: row_stats_combine_kernel<16><<<grid, 256, 0, stream>>>(pp, 16, rows, eps, mean, rstd); break;
+    case 32: row_stats_combine_kernel<32><<<grid, 256, 0, stream>>>(pp, 32, rows, eps, mean, rstd); break;
+    default: row_stats_combine_kernel<0><<<grid, 256, 0, stream>>>(pp, d / 64, rows, eps, mean, rstd);
+  }
   return hipGetLastError();
 }
 
