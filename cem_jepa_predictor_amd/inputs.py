@@ -107,6 +107,10 @@ WORKLOADS: Dict[str, Workload] = {
     # difference from the plain model.
     "shallow_fp8": Workload("shallow_fp8", ModelConfig("shallow_fp8", 1, 512, 8, 2048, 64, 512, "fp8", 1),
                             PlanConfig(16, 4, 2, 1)),
+    # bf16 at d_model 768 (12 heads): three 256-column output tiles per residual
+    # GEMM, so the LayerNorm statistics come in 12 pieces of 64 columns per row.
+    "wide768": Workload("wide768", ModelConfig("wide768", 2, 768, 12, 3072, 16, 128, "bf16", 2),
+                        PlanConfig(32, 4, 2, 2)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
     # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.
