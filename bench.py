@@ -137,6 +137,93 @@ def summarize_traffic(fetch: str, write: str, copy_fetch: str, copy_write: str,
               f"GEMM sources sha256 {gemm_sources_sha256()}")
 
 
+def summarize_sq(path: str) -> None:
+    """Per-kernel shader-engine utilization from one rocprofv3 --pmc pass over
+    SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS SQ_WAIT_INST_LDS
+    SQ_WAIT_INST_ANY SQ_VALU_MFMA_BUSY_CYCLES SQ_LDS_BANK_CONFLICT GRBM_GUI_ACTIVE (sums over
+    each kernel's dispatches; 256 CUs of 4 SIMDs, GRBM_GUI_ACTIVE summed over the 8 XCDs):
+    VALU busy = 4 SQ_ACTIVE_INST_VALU / (1024 GRBM_GUI_ACTIVE / 8), MFMA busy =
+    SQ_VALU_MFMA_BUSY_CYCLES / (1024 GRBM_GUI_ACTIVE / 8), waiting = SQ_WAIT_INST_ANY /
+    SQ_WAVE_CYCLES."""
+    import collections
+    import csv
+
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(set)
+    short = lambda k: k.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")  # noqa: E731
+    for r in csv.DictReader(open(path)):
+        k = short(r["Kernel_Name"])
+        agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k].add(r["Dispatch_Id"])
+    print("| kernel | dispatches | VALU busy | MFMA busy | wave cycles waiting (any) | of which on LDS "
+          "| LDS bank-conflict cycles per dispatch |")
+    print("|---|---:|---:|---:|---:|---:|---:|")
+    for k in sorted(agg, key=lambda k: -agg[k]["GRBM_GUI_ACTIVE"]):
+        a, n = agg[k], len(disp[k])
+        g = 1024 * a["GRBM_GUI_ACTIVE"] / 8
+        if g <= 0:
+            continue
+        wc = a["SQ_WAVE_CYCLES"] or 1.0
+        print(f"| `{k}` | {n} | {4 * a['SQ_ACTIVE_INST_VALU'] / g:.2f} | {a['SQ_VALU_MFMA_BUSY_CYCLES'] / g:.2f} "
+              f"| {a['SQ_WAIT_INST_ANY'] / wc:.2f} | {a['SQ_WAIT_INST_LDS'] / wc:.3f} "
+              f"| {a['SQ_LDS_BANK_CONFLICT'] / n:.3g} |")
+
+
+def summarize_path(path: str, workload: str = "vjepa2ac") -> None:
+    """Per-kernel memory-path figures from one rocprofv3 --pmc pass over
+    TCP_TCC_READ_REQ_LATENCY_sum TCP_TCC_READ_REQ_sum TCP_PENDING_STALL_CYCLES_sum TCC_HIT_sum
+    TCC_MISS_sum TA_TA_BUSY_sum TA_BUFFER_READ_LDS_WAVEFRONTS_sum TD_TD_BUSY_sum TD_TC_STALL_sum
+    GRBM_GUI_ACTIVE (sums over each kernel's dispatches; durations from the dispatches' own
+    timestamps).  L2 hit rate = hits / (hits + misses); L1->L2 read latency = latency sum / read
+    requests; TA, TD and TCP figures = their cycles / (256 units x GRBM_GUI_ACTIVE / 8); clock =
+    GRBM_GUI_ACTIVE / 8 per dispatch over its duration.  For the layer GEMMs of `workload` (M = N B
+    rows), bytes per clock per CU = (LDS-DMA wavefronts x 1 KB + residual rows read + bf16 results
+    and row statistics written) / (cycles x 256)."""
+    import collections
+    import csv
+
+    from cem_jepa_predictor_amd import inputs
+
+    wl = inputs.WORKLOADS[workload]
+    m = wl.model
+    M = wl.plan.n_samples * m.block_tokens
+    d, F = m.d_model, m.d_mlp
+    # results written + residual rows read per dispatch, averaged over the launches of each kind
+    # output / down: residual read + result write + the LayerNorm piece statistics (M d / 8 bytes;
+    # every residual launch but the last layer's MLP down writes them)
+    extra = {"gemm_bf16_kernel<2, false, false>": 2 * (M * d * 2) + (M * d // 8 if m.dtype == "bf16" and d % 256 == 0 else 0),
+             "gemm_bf16_kernel<1, false, true>": M * F * 2,               # MLP up
+             "gemm_bf16_kernel<0, false, true>": M * 3 * d * 2}           # q|k|v
+    agg = collections.defaultdict(lambda: collections.defaultdict(float))
+    disp = collections.defaultdict(dict)
+    short = lambda k: k.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")  # noqa: E731
+    for r in csv.DictReader(open(path)):
+        k = short(r["Kernel_Name"])
+        agg[k][r["Counter_Name"]] += float(r["Counter_Value"])
+        disp[k][r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    print("| kernel | dispatches | mean duration (us) | clock (MHz) | L2 hit rate | L1→L2 read latency (cycles) "
+          "| TA busy | TD busy | TD waiting for L2 data | L1 stalled on pending L2 data "
+          "| operand + residual + result bytes per clock per CU |")
+    print("|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|---:|")
+    for k in sorted(agg, key=lambda k: -agg[k]["GRBM_GUI_ACTIVE"]):
+        a, n = agg[k], len(disp[k])
+        cyc = a["GRBM_GUI_ACTIVE"] / 8                       # per-XCD cycles, all dispatches
+        if cyc <= 0:
+            continue
+        dur = sum(disp[k].values())
+        hits, miss = a["TCC_HIT_sum"], a["TCC_MISS_sum"]
+        reqs = a["TCP_TCC_READ_REQ_sum"] or 1.0
+        units = 256 * cyc
+        bpc = "—"
+        for kind, eb in extra.items():
+            if k.endswith(kind):
+                bpc = f"{(a['TA_BUFFER_READ_LDS_WAVEFRONTS_sum'] * 1024 + eb * n) / units:.1f}"
+        print(f"| `{k}` | {n} | {dur / n * 1e6:.1f} | {cyc / dur / 1e6:.0f} | {hits / max(hits + miss, 1):.2f} "
+              f"| {a['TCP_TCC_READ_REQ_LATENCY_sum'] / reqs:.0f} | {a['TA_TA_BUSY_sum'] / units:.2f} "
+              f"| {a['TD_TD_BUSY_sum'] / units:.2f} | {a['TD_TC_STALL_sum'] / units:.2f} "
+              f"| {a['TCP_PENDING_STALL_CYCLES_sum'] / units:.2f} | {bpc} |")
+
+
 def eprint(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -291,7 +378,19 @@ def main() -> int:
                          "WRITE_SIZE of the bench, the same of the --copy-bytes run, and "
                          "optionally the --kernel-trace --stats CSV of the bench (mean duration, "
                          "GB/s), then exit")
+    ap.add_argument("--summarize-sq", metavar="COUNTER_CSV",
+                    help="print per-kernel VALU / MFMA busy and wait shares from a rocprofv3 --pmc "
+                         "pass over the SQ counters (see summarize_sq), then exit")
+    ap.add_argument("--summarize-path", metavar="COUNTER_CSV",
+                    help="print per-kernel memory-path figures from a rocprofv3 --pmc pass over the "
+                         "TCP / TCC / TA / TD counters (see summarize_path) for --workload, then exit")
     args = ap.parse_args()
+    if args.summarize_path:
+        summarize_path(args.summarize_path, args.workload)
+        return 0
+    if args.summarize_sq:
+        summarize_sq(args.summarize_sq)
+        return 0
     if args.summarize_stats:
         summarize_stats(args.summarize_stats)
         return 0
