@@ -111,6 +111,10 @@ WORKLOADS: Dict[str, Workload] = {
     # GEMM, so the LayerNorm statistics come in 12 pieces of 64 columns per row.
     "wide768": Workload("wide768", ModelConfig("wide768", 2, 768, 12, 3072, 16, 128, "bf16", 2),
                         PlanConfig(32, 4, 2, 2)),
+    # One bf16 layer at d_model 2048 (32 heads): the MLP-up LayerNorm's statistics
+    # from the output projection's epilogue in 32 pieces per row.
+    "wide2048": Workload("wide2048", ModelConfig("wide2048", 1, 2048, 32, 2048, 16, 64, "bf16", 1),
+                         PlanConfig(16, 4, 2, 1)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
     # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.

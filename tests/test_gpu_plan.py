@@ -46,10 +46,11 @@ def gpu_rollout(name, actions):
 
 
 # small with n = 3 and 5 (M = 198, 330 rows): the last rows of each GEMM fill an 8-row piece only
-# partly (6 and 2 rows), in the residual kind's buffer-bounded epilogue as well.  wide768: the
-# LayerNorm statistics of d = 768 rows in 12 pieces (small: 8, oddk: a statistics pass of its own)
+# partly (6 and 2 rows), in the residual kind's buffer-bounded epilogue as well.  wide768 and
+# wide2048: the LayerNorm statistics of d = 768 and 2048 rows in 12 and 32 pieces (small: 8, the
+# V-JEPA2-AC shape: 16, oddk: a statistics pass of its own)
 @pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("small", 3), ("small", 5),
-                                    ("oddk", 9), ("small_fp8", 12), ("wide768", 12)])
+                                    ("oddk", 9), ("small_fp8", 12), ("wide768", 12), ("wide2048", 9)])
 def test_rollout_matches_oracle(gpu_lib, name, n):
     from cem_jepa_predictor_amd import inputs
 
