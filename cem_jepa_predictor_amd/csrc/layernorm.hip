@@ -30,10 +30,29 @@ template <> struct Pair<bf16> {
   __device__ static __forceinline__ V pack(float a, float b) { return pack_bf16x2(a, b); }
 };
 
+// Sum and max over the 64 lanes, the same value in every lane, without LDS: lanes
+// combine in pairs through DPP quad permutations ([1,0,3,2], [2,3,0,1]) and the
+// half-row and row mirrors (within 16 lanes), then across 16-lane rows through
+// v_permlane16_swap and across the two halves through v_permlane32_swap.  Each step
+// combines two lanes' values, which both lanes get bit for bit (the operation is
+// commutative).
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float v, Op op) {
+  v = op(v, dpp_f<0xb1>(v));    // quad_perm [1,0,3,2]
+  v = op(v, dpp_f<0x4e>(v));    // quad_perm [2,3,0,1]
+  v = op(v, dpp_f<0x141>(v));   // row_half_mirror
+  v = op(v, dpp_f<0x140>(v));   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = op(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return op(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  return wave_reduce(v, [](float x, float y) { return x + y; });
 }
 
 template <int NCH, typename T>
@@ -127,9 +146,7 @@ __global__ __launch_bounds__(256) void layernorm_bf16x8_kernel(const bf16* __res
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  return wave_reduce(v, [](float x, float y) { return fmaxf(x, y); });
 }
 
 // LayerNorm of bf16 rows (d = 512 * NC, one wave per row, 8 consecutive values per
