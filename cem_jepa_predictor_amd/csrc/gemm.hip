@@ -802,9 +802,10 @@ hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int
                             const Epilogue& epi, hipStream_t stream) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (K <= 0 || K % BK != 0) return hipErrorInvalidValue;
-  // row statistics come from the staged epilogue, which every tile must take
+  // row statistics come from the staged epilogue, which every tile must take; their
+  // buffer resources count bytes in 32 bits (8 per row)
   if (epi.stats && !(epi.residual && N % BN == 0 && epi.split >= N && (epi.ld0 & 7) == 0 &&
-                     epi.rows.group > M && ((uintptr_t)epi.c0 & 15) == 0))
+                     epi.rows.group > M && ((uintptr_t)epi.c0 & 15) == 0 && M < (1 << 28)))
     return hipErrorInvalidValue;
   int cus = 0;
   const hipError_t ce = cu_count(&cus);

@@ -63,7 +63,7 @@ hipError_t launch_quantize_rows_fp8(const float* x, int rows, int cols, uint8_t*
 // out = epilogue(A[M, K] @ Bt[N, K]^T); N % 4 == 0; bf16 (MFMA): K % 64 == 0
 // (hipErrorInvalidValue otherwise); fp32: K % 16 == 0.  epi.stats (bf16 residual
 // kind only) also needs N % 256 == 0, one output (split >= N) with ld0 % 8 == 0 and
-// a 16-byte aligned c0, and identity rows; the other launchers reject it.
+// a 16-byte aligned c0, identity rows and M < 2^28; the other launchers reject it.
 hipError_t launch_gemm_bf16(const bf16* A, int lda, const bf16* Bt, int ldb, int M, int N,
                             int K, const Epilogue& epi, hipStream_t stream);
 hipError_t launch_gemm_f32(const float* A, int lda, const float* Bt, int ldb, int M, int N,

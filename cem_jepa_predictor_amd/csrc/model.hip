@@ -363,7 +363,8 @@ Status model_create(const cem_model_desc& d, const float* host_w, int device, ce
   const size_t o_f0 = al.take(P * D * es), o_zobs = al.take(P * E * es);
   const size_t o_h8 = al.take(m->fp8 ? rows * D : 0), o_hs = al.take(m->fp8 ? rows * 4 : 0);
   const size_t o_stats = al.take(fold * 2 * rows * 4);
-  const size_t parts = (fold && D % 256 == 0) ? 1 : 0;   // residual GEMMs write LN statistics
+  // residual GEMMs write LN statistics (their launcher takes up to 2^28 rows)
+  const size_t parts = (fold && D % 256 == 0 && rows < (size_t(1) << 28)) ? 1 : 0;
   const size_t o_parts = al.take(parts * (D / 64) * rows * 8);
   e = hipMalloc(&m->arena, al.off);
   if (e != hipSuccess) return fail(hip_status(e, "hipMalloc(workspace)"));
