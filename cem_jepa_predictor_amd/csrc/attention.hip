@@ -95,28 +95,54 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4, 4))) voi
   const int vr4 = (lane >> 2) & 3, vc4 = lane & 3;   // transposing-read source slot
   const float sl2 = p.scale * 1.4426950408889634f;   // softmax in base 2
 
+  // Compact layer-0 source (AttnArgs::qkv_c): row r of this candidate is row crow(r) of
+  // the compact q|k|v block (3 d wide): its action row after every problem's shared rows,
+  // the shared rows of its problem otherwise.
+  const bool cmp = p.qkv_c != nullptr;
+  const int ldc = 3 * p.d;
+  const int c_act = p.c_problems * (B - 1) + n;
+  const int c_sh = cmp ? (n / p.c_n_per) * (B - 1) - 1 : 0;
+  auto crow = [&](int r) { return r == 0 ? c_act : c_sh + r; };
+
   // ---- K and V rows 0 .. kpad-1 of this (candidate, head) -> LDS, 8 rows (1 KB) per
   // instruction; LDS row r holds 16-byte chunk c at c ^ (r & 7)
   {
-    const bf16* kvb = static_cast<const bf16*>(p.kv[0]) + (long long)n * B * p.ldkv + h * kDh;
-    const int bytes = (B - 1) * p.ldkv * 2 + kDh * 2;
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb), (short)0, bytes, 0x00020000);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb + p.d), (short)0, bytes, 0x00020000);
     const int rows8 = kpad >> 3, ninstr = 2 * rows8;
     const int lrow = lane >> 3, lch = (lane & 7) ^ (lane >> 3);
-    for (int t = wave; t < ninstr; t += 8) {
-      const bool isv = t >= rows8;
-      const int r0 = 8 * (isv ? t - rows8 : t);
-      const int voff = (r0 + lrow) * p.ldkv * 2 + lch * 16;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_ptr_t)((isv ? v_lds : k_lds) + r0 * 128), 16, voff, 0, 0, 0);
+    if (cmp) {
+      // rows past B take an offset beyond the resource: they read as zero
+      const bf16* kb = static_cast<const bf16*>(p.qkv_c) + p.d + h * kDh;
+      const int bytes = (p.c_problems * (B - 1) + p.n - 1) * ldc * 2 + kDh * 2;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kb), (short)0, bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kb + p.d), (short)0, bytes, 0x00020000);
+      for (int t = wave; t < ninstr; t += 8) {
+        const bool isv = t >= rows8;
+        const int r0 = 8 * (isv ? t - rows8 : t), r = r0 + lrow;
+        const int voff = r < B ? crow(r) * ldc * 2 + lch * 16 : 0x7ffffff0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_ptr_t)((isv ? v_lds : k_lds) + r0 * 128), 16, voff, 0, 0, 0);
+      }
+    } else {
+      const bf16* kvb = static_cast<const bf16*>(p.kv[0]) + (long long)n * B * p.ldkv + h * kDh;
+      const int bytes = (B - 1) * p.ldkv * 2 + kDh * 2;
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb), (short)0, bytes, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(kvb + p.d), (short)0, bytes, 0x00020000);
+      for (int t = wave; t < ninstr; t += 8) {
+        const bool isv = t >= rows8;
+        const int r0 = 8 * (isv ? t - rows8 : t);
+        const int voff = (r0 + lrow) * p.ldkv * 2 + lch * 16;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(isv ? rv : rk, (lds_ptr_t)((isv ? v_lds : k_lds) + r0 * 128), 16, voff, 0, 0, 0);
+      }
     }
   }
-  const bf16* qbase = static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
+  const bf16* qbase = cmp ? static_cast<const bf16*>(p.qkv_c) + h * kDh
+                          : static_cast<const bf16*>(p.q) + (long long)n * B * p.ldq + h * kDh;
+  const int qld = cmp ? ldc : p.ldq;
   auto load_q = [&](int tile, bf16x8_t q[2]) {
-    const int qr = min(tile * 16 + ql, B - 1);
+    const int qi = min(tile * 16 + ql, B - 1);
+    const int qr = cmp ? crow(qi) : qi;
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      q[s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * p.ldq + 32 * s + 8 * g);
+      q[s] = *reinterpret_cast<const bf16x8_t*>(qbase + (long long)qr * qld + 32 * s + 8 * g);
   };
   bf16x8_t qf[2], qn[2];
   load_q(wave, qf);
@@ -466,6 +492,10 @@ hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream) {
   if (a.n <= 0) return hipSuccess;
   const int kt = (a.B + 15) / 16;
   if (kt < 1 || kt > kMaxKeyTiles) return hipErrorInvalidValue;
+  if (a.qkv_c && (a.nblk != 1 || a.B < 2 || a.c_problems <= 0 || a.c_n_per <= 0 ||
+                  a.n != a.c_problems * a.c_n_per ||
+                  ((long long)a.c_problems * (a.B - 1) + a.n) * 3 * a.d * 2 >= 0x7ffffff0LL))
+    return hipErrorInvalidValue;
   if (a.nblk == 1)
     launch_kt(kt, a, stream, KtRange{});
   else

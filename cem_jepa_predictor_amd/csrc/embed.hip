@@ -69,7 +69,32 @@ __global__ __launch_bounds__(256) void broadcast_frame_kernel(const T* __restric
   *reinterpret_cast<uint4*>(dst) = *reinterpret_cast<const uint4*>(f0 + i);
 }
 
+// Layer 0 of the first frame block: the rows every candidate of a problem shares and the
+// candidates' own action rows, packed into one compact block (16 bytes a thread).
+__global__ __launch_bounds__(256) void gather_layer0_kernel(const bf16* __restrict__ x, int B, int d,
+                                                            int problems, int n_per, long long count,
+                                                            bf16* __restrict__ xc) {
+  const long long i = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+  if (i >= count) return;
+  const int r = (int)(i / d), j = (int)(i % d);
+  const int shared = problems * (B - 1);
+  const long long src = r < shared ? (long long)(r / (B - 1)) * n_per * B + 1 + r % (B - 1)
+                                   : (long long)(r - shared) * B;
+  *reinterpret_cast<uint4*>(xc + i) = *reinterpret_cast<const uint4*>(x + src * d + j);
+}
+
 }  // namespace
+
+hipError_t launch_gather_layer0(const bf16* x, int B, int d, int problems, int n_per, int N,
+                                bf16* xc, hipStream_t stream) {
+  if (N <= 0) return hipSuccess;
+  if (problems <= 0 || n_per <= 0 || N != problems * n_per || B < 2 || d <= 0 || d % 8 != 0)
+    return hipErrorInvalidValue;
+  const long long count = ((long long)problems * (B - 1) + N) * d;
+  gather_layer0_kernel<<<(unsigned)((count / 8 + 255) / 256), 256, 0, stream>>>(x, B, d, problems,
+                                                                              n_per, count, xc);
+  return hipGetLastError();
+}
 
 template <typename T>
 hipError_t launch_convert(const float* in, T* out, long long count, hipStream_t stream) {

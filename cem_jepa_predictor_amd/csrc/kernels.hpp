@@ -35,6 +35,13 @@ hipError_t launch_embed_action_state(const float* X, int N, int H, int t, int A,
 template <typename T>
 hipError_t launch_broadcast_frame(const T* f0, int P, int d, T* x, int N, int B, int n_per,
                                   hipStream_t stream);
+// The rows of the first frame block that layer 0 needs once each, gathered from x
+// [N*B, d] into xc [problems (B - 1) + N, d]: problem b's shared rows (rows 1 .. B-1 of
+// its first candidate b n_per: the state token and the frame tokens) at b (B - 1) + j,
+// then candidate k's action row (row k B) at problems (B - 1) + k.  N = problems n_per,
+// d % 8 == 0.
+hipError_t launch_gather_layer0(const bf16* x, int B, int d, int problems, int n_per, int N,
+                                bf16* xc, hipStream_t stream);
 
 // --- layernorm.hip -----------------------------------------------------------
 // y[r] = (x[in_rows(r)] - mean) * rsqrt(var + eps) * g + b, fp32 statistics.
@@ -95,6 +102,12 @@ struct AttnArgs {
   int ldq, ldkv, ldo;
   int n, heads, dh, d, B, nblk;
   float scale;
+  // bf16, nblk == 1, optional: q, k and v of every row come from the compact q|k|v
+  // block [c_problems (B - 1) + n, 3 d] of the gathered layer-0 rows (launch_gather_layer0
+  // order): row 0 of candidate i at c_problems (B - 1) + i, row r >= 1 at
+  // (i / c_n_per) (B - 1) + r - 1; q, kv and ldq / ldkv are then unused.
+  const void* qkv_c;
+  int c_problems, c_n_per;
 };
 hipError_t launch_attention_bf16(const AttnArgs& a, hipStream_t stream);
 hipError_t attention_init();   // one-time dynamic-LDS attribute

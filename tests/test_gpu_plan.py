@@ -48,15 +48,21 @@ def gpu_rollout(name, actions):
 # small with n = 3 and 5 (M = 198, 330 rows): the last rows of each GEMM fill an 8-row piece only
 # partly (6 and 2 rows), in the residual kind's buffer-bounded epilogue as well.  wide768 and
 # wide2048: the LayerNorm statistics of d = 768 and 2048 rows in 12 and 32 pieces (small: 8, the
-# V-JEPA2-AC shape: 16, oddk: a statistics pass of its own)
-@pytest.mark.parametrize("name,n", [("tiny", 64), ("tiny", 5), ("small", 12), ("small", 3), ("small", 5),
-                                    ("oddk", 9), ("small_fp8", 12), ("wide768", 12), ("wide2048", 9)])
-def test_rollout_matches_oracle(gpu_lib, name, n):
+# V-JEPA2-AC shape: 16, oddk: a statistics pass of its own).  Horizon 1 on the bf16 models
+# (small, wide2048): layer 0 projects each problem's shared rows once and the candidates'
+# action rows once, in one compact block the attention reads from.
+@pytest.mark.parametrize("name,n,horizon", [("tiny", 64, None), ("tiny", 5, None), ("small", 12, None),
+                                            ("small", 3, None), ("small", 5, None), ("small", 12, 1),
+                                            ("small", 3, 1), ("oddk", 9, None), ("oddk", 9, 1),
+                                            ("small_fp8", 12, None), ("wide768", 12, None),
+                                            ("wide2048", 9, None)])
+def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
     from cem_jepa_predictor_amd import inputs
 
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
-    log(f"rollout {name} n={n} H={wl.plan.horizon}")
-    actions = inputs.make_actions(n, wl.plan.horizon, seed=n)
+    H = horizon or wl.plan.horizon
+    log(f"rollout {name} n={n} H={H}")
+    actions = inputs.make_actions(n, H, seed=n)
     got = gpu_rollout(name, actions)
     pred = oracle_predictor(name)
     want = pred.rollout_cached(actions, z_obs, s0)
@@ -191,9 +197,11 @@ def test_plan_graph_equals_eager_and_is_deterministic(gpu_lib, name):
     assert not np.array_equal(a["x"], d["x"])
 
 
-def test_rollout_is_invariant_to_candidate_chunking(gpu_lib):
+@pytest.mark.parametrize("horizon", [None, 1])
+def test_rollout_is_invariant_to_candidate_chunking(gpu_lib, horizon):
     """Same seeds give the same answer however candidates are grouped (cf. plans identical
-    at 1, 2, 4 and 8 GPUs)."""
+    at 1, 2, 4 and 8 GPUs).  At horizon 1 the groups also change the compact layer-0 block
+    (shared rows once, then each group's action rows)."""
     import torch
     from cem_jepa_predictor_amd import _lib
 
@@ -201,7 +209,7 @@ def test_rollout_is_invariant_to_candidate_chunking(gpu_lib):
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
     from cem_jepa_predictor_amd import inputs
 
-    actions = inputs.make_actions(64, wl.plan.horizon, seed=11)
+    actions = inputs.make_actions(64, horizon or wl.plan.horizon, seed=11)
     full = gpu_rollout(name, actions)
     parts = np.concatenate([gpu_rollout(name, actions[i:i + 16]) for i in range(0, 64, 16)])
     np.testing.assert_array_equal(full, parts)
@@ -267,12 +275,12 @@ def test_warm_started_closed_loop_lockstep(gpu_lib, floor):
         np.testing.assert_array_equal(mu[0], out["mu_out"][1])
 
 
-def _problems(name, batch):
+def _problems(name, batch, horizon=None):
     """Per-problem inputs: problem 0 is the workload's own, the others differ in
     observation, goal, state and starting Gaussian."""
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
     pc, m = wl.plan, wl.model
-    H, A = pc.horizon, m.action_dim
+    H, A = horizon or pc.horizon, m.action_dim
     rng = np.random.default_rng(17)
     zo = [z_obs] + [rng.standard_normal(z_obs.shape).astype(np.float32) for _ in range(batch - 1)]
     zg = [z_goal] + [rng.standard_normal(z_goal.shape).astype(np.float32) for _ in range(batch - 1)]
@@ -285,10 +293,12 @@ def _problems(name, batch):
 
 
 # sweep_400 x 2: two V-JEPA2-AC-shaped problems of 400 candidates in one 800-candidate batch
-# (M = 206,400 rows), as the benchmark's fleet-batching rows run it
-@pytest.mark.parametrize("name,batch,use_graph", [("tiny", 3, True), ("small", 2, True), ("tiny", 2, False),
-                                                  ("sweep_400", 2, True)])
-def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
+# (M = 206,400 rows), as the benchmark's fleet-batching rows run it.  small at horizon 1: three
+# problems' shared layer-0 rows in one compact block
+@pytest.mark.parametrize("name,batch,use_graph,horizon", [("tiny", 3, True, None), ("small", 2, True, None),
+                                                          ("tiny", 2, False, None), ("small", 3, True, 1),
+                                                          ("sweep_400", 2, True, None)])
+def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph, horizon):
     """Fleet batching (page section 06 C): a batched plan of several problems in one
     predictor batch gives each problem exactly its own cem_plan result (plan id
     + b), trace included."""
@@ -297,9 +307,10 @@ def test_plan_batched_equals_independent_plans(gpu_lib, name, batch, use_graph):
 
     wl = workload_data(name)[0]
     pc, m = wl.plan, wl.model
-    N, K, R, H, A = pc.n_samples, pc.n_elites, min(pc.rounds, 3), pc.horizon, m.action_dim
-    log(f"batched plan {name}: {batch} problems x N={N}, R={R}, graph={use_graph}")
-    zo, zg, st, mu, sg = _problems(name, batch)
+    N, K, R, A = pc.n_samples, pc.n_elites, min(pc.rounds, 3), m.action_dim
+    H = horizon or pc.horizon
+    log(f"batched plan {name}: {batch} problems x N={N}, R={R}, H={H}, graph={use_graph}")
+    zo, zg, st, mu, sg = _problems(name, batch, H)
     model = gpu_model(name, batch * N)
     kw = dict(n_samples=N, n_elites=K, rounds=R, horizon=H, seed=pc.seed, clamp_lo=pc.clamp_lo,
               clamp_hi=pc.clamp_hi, use_graph=use_graph)
