@@ -478,16 +478,17 @@ void* kv_slot(cem_model* m, int l, int tau, int horizon) {
   return static_cast<uint8_t*>(m->kv) + slot * (size_t)m->rows_max * 2 * m->desc.d_model * m->esz;
 }
 
-// Layer 0 of the first frame block at horizon 1 (bf16 models, LayerNorm folded): every
-// candidate of a problem shares that problem's state token and frame tokens (rows
-// 1 .. B-1), so their LayerNorm statistics and q|k|v projection are the same rows
-// computed n_per times over.  They are computed once per problem instead, and each
-// candidate's action row once, in one compact block of problems (B - 1) + n rows that
-// the attention reads q, k and v from.  Every row goes through the same kernels and
-// arithmetic as in the full batch, so the results are unchanged bit for bit.  Horizon
-// > 1 keeps the full layer-0 K/V of the first block in the KV cache for later steps.
+// Layer 0 of the first frame block at horizon 1 (bf16 models with the LayerNorm folded,
+// and fp8-projection models): every candidate of a problem shares that problem's state
+// token and frame tokens (rows 1 .. B-1), so their LayerNorm statistics and q|k|v
+// projection are the same rows computed n_per times over.  They are computed once per
+// problem instead, and each candidate's action row once, in one compact block of
+// problems (B - 1) + n rows that the attention reads q, k and v from.  Every row goes
+// through the same kernels and arithmetic as in the full batch, so the results are
+// unchanged bit for bit.  Horizon > 1 keeps the full layer-0 K/V of the first block in
+// the KV cache for later steps.
 bool layer0_compact(const cem_model* m, int n, int n_per, int H) {
-  if (!m->ln_fold || m->fp8 || H != 1 || n_per <= 0 || n % n_per != 0 || m->B < 2) return false;
+  if (!(m->ln_fold || m->fp8) || H != 1 || n_per <= 0 || n % n_per != 0 || m->B < 2) return false;
   const long long rows = (long long)(n / n_per) * (m->B - 1) + n;
   // compact rows go to the q buffer ([rows_max, d]) and their q|k|v to the current KV slot
   // ([rows_max, 2 d]); the attention addresses that block with 32-bit byte offsets
@@ -532,21 +533,28 @@ hipError_t enqueue_rollout(cem_model* m, const float* X, int n, int H, const flo
     for (int l = 0; l < d.layers; ++l) {
       const LayerW& w = m->layers[l];
       void* qkv_c = nullptr;   // compact layer-0 q|k|v block (layer0_compact)
-      if (m->fp8) {
-        RUN(launch_layernorm_fp8(static_cast<const bf16*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
-                                 w.ln1_b, d.ln_eps, m->h8, m->hs, st));
-        RUN(gemm8(m, m->h8, D, w.w_qkv_t, D, rows, 3 * D, D, m->hs, w.ws_qkv,
-                  epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
-      } else if (m->ln_fold && l == 0 && t == 0 && layer0_compact(m, n, n_per, H)) {
+      if (l == 0 && t == 0 && layer0_compact(m, n, n_per, H)) {
         const int problems = n / n_per, rc = problems * (B - 1) + n;
         bf16* const xc = static_cast<bf16*>(m->q);
         qkv_c = kv_slot(m, 0, 0, H);
         RUN(launch_gather_layer0(static_cast<const bf16*>(m->x), B, D, problems, n_per, n, xc, st));
-        RUN(launch_row_stats(xc, rc, D, d.ln_eps, m->ln_stats + rc, m->ln_stats, st));
-        RUN(timer_start(m, st, 2.0 * rc * (3.0 * D) * D));
-        RUN(launch_gemm_bf16_rows(xc, D, static_cast<const bf16*>(w.w_qkv_t), D, rc, 3 * D, D,
-                                  m->ln_stats, epi(w.b_qkv, qkv_c, 3 * D, 3 * D), st));
-        RUN(timer_stop(m, st));
+        if (m->fp8) {
+          RUN(launch_layernorm_fp8(xc, rc, D, RowMap::identity(), w.ln1_g, w.ln1_b, d.ln_eps, m->h8,
+                                   m->hs, st));
+          RUN(gemm8(m, m->h8, D, w.w_qkv_t, D, rc, 3 * D, D, m->hs, w.ws_qkv,
+                    epi(w.b_qkv, qkv_c, 3 * D, 3 * D), st));
+        } else {
+          RUN(launch_row_stats(xc, rc, D, d.ln_eps, m->ln_stats + rc, m->ln_stats, st));
+          RUN(timer_start(m, st, 2.0 * rc * (3.0 * D) * D));
+          RUN(launch_gemm_bf16_rows(xc, D, static_cast<const bf16*>(w.w_qkv_t), D, rc, 3 * D, D,
+                                    m->ln_stats, epi(w.b_qkv, qkv_c, 3 * D, 3 * D), st));
+          RUN(timer_stop(m, st));
+        }
+      } else if (m->fp8) {
+        RUN(launch_layernorm_fp8(static_cast<const bf16*>(m->x), rows, D, RowMap::identity(), w.ln1_g,
+                                 w.ln1_b, d.ln_eps, m->h8, m->hs, st));
+        RUN(gemm8(m, m->h8, D, w.w_qkv_t, D, rows, 3 * D, D, m->hs, w.ws_qkv,
+                  epi(w.b_qkv, m->q, D, D, kv_slot(m, l, t, H), 2 * D), st));
       } else if (m->ln_fold) {
         // layer 0's input rows come from the token embedding, the others' from a residual GEMM
         RUN(gemm_ln(m, m->x, D, w.w_qkv_t, D, rows, 3 * D, D,

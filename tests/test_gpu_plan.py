@@ -48,13 +48,14 @@ def gpu_rollout(name, actions):
 # small with n = 3 and 5 (M = 198, 330 rows): the last rows of each GEMM fill an 8-row piece only
 # partly (6 and 2 rows), in the residual kind's buffer-bounded epilogue as well.  wide768 and
 # wide2048: the LayerNorm statistics of d = 768 and 2048 rows in 12 and 32 pieces (small: 8, the
-# V-JEPA2-AC shape: 16, oddk: a statistics pass of its own).  Horizon 1 on the bf16 models
-# (small, wide2048): layer 0 projects each problem's shared rows once and the candidates'
-# action rows once, in one compact block the attention reads from.
+# V-JEPA2-AC shape: 16, oddk: a statistics pass of its own).  Horizon 1 on the bf16 and fp8
+# models (small, oddk, small_fp8, wide2048): layer 0 projects each problem's shared rows once
+# and the candidates' action rows once, in one compact block the attention reads from.
 @pytest.mark.parametrize("name,n,horizon", [("tiny", 64, None), ("tiny", 5, None), ("small", 12, None),
                                             ("small", 3, None), ("small", 5, None), ("small", 12, 1),
                                             ("small", 3, 1), ("oddk", 9, None), ("oddk", 9, 1),
-                                            ("small_fp8", 12, None), ("wide768", 12, None),
+                                            ("small_fp8", 12, None), ("small_fp8", 12, 1),
+                                            ("wide768", 12, None),
                                             ("wide2048", 9, None)])
 def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
     from cem_jepa_predictor_amd import inputs
