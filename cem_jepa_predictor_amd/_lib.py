@@ -50,7 +50,7 @@ class Params(ctypes.Structure):
                 ("rounds", ctypes.c_int32), ("horizon", ctypes.c_int32),
                 ("clamp_lo", ctypes.c_float), ("clamp_hi", ctypes.c_float),
                 ("seed", ctypes.c_uint64), ("plan_id", ctypes.c_uint32),
-                ("use_graph", ctypes.c_int32)]
+                ("use_graph", ctypes.c_int32), ("first_round", ctypes.c_uint32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -239,10 +239,11 @@ class Model:
     def plan(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
              n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,
              clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True, stream=None,
-             noalloc: bool = False):
+             noalloc: bool = False, first_round: int = 0):
         """cem_plan (or, with noalloc, cem_plan_noalloc: the plan state in the library's
         per-device scratch, nothing allocated, kernels enqueued directly, the model's
-        trace untouched)."""
+        trace untouched).  first_round > 0 resumes a plan after that many rounds from
+        the mu and sigma it returned."""
         c = self.cfg
         pe, ha = (c.patches, c.enc_dim), (horizon, c.action_dim)
         ptrs = _args((z_obs, "z_obs", _f32(), pe), (z_goal, "z_goal", _f32(), pe),
@@ -250,7 +251,7 @@ class Model:
                      (sigma, "sigma", _f32(), ha), (action, "action", _f32(), (c.action_dim,)),
                      (best_idx, "best_idx", _i32(), (1,), True))
         p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
-                   1 if use_graph else 0)
+                   1 if use_graph else 0, first_round)
         with _OnStream(stream) as st:
             if noalloc:
                 _check(load().cem_plan_noalloc(self.handle, ctypes.byref(p), *ptrs, st))
@@ -261,7 +262,7 @@ class Model:
     def plan_batched(self, z_obs, z_goal, s0, mu, sigma, action, best_idx=None, *, n_samples: int,
                      n_elites: int, rounds: int, horizon: int, seed: int, plan_id: int = 0,
                      clamp_lo: float = -1.0, clamp_hi: float = 1.0, use_graph: bool = True,
-                     stream=None):
+                     stream=None, first_round: int = 0):
         """cem_plan_batched: z_obs/z_goal [b, P, E], s0 [b, S], mu/sigma [b, H, A],
         action [b, A], best_idx [b]; problem i plans with plan id plan_id + i."""
         c = self.cfg
@@ -274,7 +275,7 @@ class Model:
                      (sigma, "sigma", _f32(), ha), (action, "action", _f32(), (b, c.action_dim)),
                      (best_idx, "best_idx", _i32(), (b,), True))
         p = Params(n_samples, n_elites, rounds, horizon, clamp_lo, clamp_hi, seed, plan_id,
-                   1 if use_graph else 0)
+                   1 if use_graph else 0, first_round)
         with _OnStream(stream) as st:
             _check(load().cem_plan_batched(self.handle, ctypes.byref(p), b, *ptrs, st))
         self._last = p

@@ -11,15 +11,16 @@ constexpr int kMaxBlocks = 8;   // frame blocks a query can attend (max horizon)
 
 // --- sampler.hip ---------------------------------------------------------
 // x[e] = clamp(mu[e % ha] + sigma[e % ha] * z[e], lo, hi), e < n * ha.
-// dev_params (nullable): uint32 {seed_lo, seed_hi, plan_id} overriding the
-// scalar arguments, so a captured graph can be re-keyed without re-capture.
+// dev_params (nullable): uint32 {seed_lo, seed_hi, plan_id, first_round} overriding
+// the key and plan id and offsetting `round`, so a captured graph can be re-keyed
+// (and a plan resumed) without re-capture.
 // batch > 1: problem b samples with mu + b ha, sigma + b ha and plan id + b into
 // x + b n ha (raw likewise), exactly as a batch-1 call with those arguments.
 hipError_t launch_sample(const float* mu, const float* sigma, int n, int ha, uint64_t seed,
                          uint32_t round, uint32_t plan_id, const uint32_t* dev_params, float lo,
                          float hi, float* x, uint32_t* raw, hipStream_t stream, int batch = 1);
 hipError_t launch_set_params(uint32_t* dev_params, uint64_t seed, uint32_t plan_id,
-                             hipStream_t stream);
+                             uint32_t first_round, hipStream_t stream);
 
 // --- embed.hip -------------------------------------------------------------
 template <typename T>

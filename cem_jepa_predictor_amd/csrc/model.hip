@@ -707,7 +707,7 @@ Status plan_with_state(cem_model* m, const PlanState& ps, bool direct, const cem
   CEM_TRY(hipMemcpyAsync(ps.s0, s0, nb * S * 4, hipMemcpyDeviceToDevice, st), "copy s0");
   CEM_TRY(hipMemcpyAsync(ps.mu_hist, mu, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy mu");
   CEM_TRY(hipMemcpyAsync(ps.sigma_hist, sigma, nb * ha * 4, hipMemcpyDeviceToDevice, st), "copy sigma");
-  CEM_TRY(launch_set_params(ps.params, p.seed, p.plan_id, st), "set params");
+  CEM_TRY(launch_set_params(ps.params, p.seed, p.plan_id, p.first_round, st), "set params");
   Status s;
   if (direct)
     s = hip_status(m->bf16 ? enqueue_plan_body<bf16>(m, ps, p, batch, st)

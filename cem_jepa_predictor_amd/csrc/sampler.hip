@@ -57,7 +57,10 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ m
                                                      uint32_t* __restrict__ raw) {
   const int c = blockIdx.x * blockDim.x + threadIdx.x;
   if (4 * c >= total) return;
-  if (dev_params) { k0 = dev_params[0]; k1 = dev_params[1]; plan_id = dev_params[2]; }
+  if (dev_params) {
+    k0 = dev_params[0]; k1 = dev_params[1]; plan_id = dev_params[2];
+    round += dev_params[3];   // the plan's first round
+  }
   // problem b of a batch: its own Gaussian and sample block, plan id + b
   const int b = blockIdx.y;
   plan_id += (uint32_t)b;
@@ -81,8 +84,9 @@ __global__ __launch_bounds__(256) void sample_kernel(const float* __restrict__ m
   }
 }
 
-__global__ void set_params_kernel(uint32_t* p, uint32_t k0, uint32_t k1, uint32_t plan_id) {
-  if (threadIdx.x == 0) { p[0] = k0; p[1] = k1; p[2] = plan_id; }
+__global__ void set_params_kernel(uint32_t* p, uint32_t k0, uint32_t k1, uint32_t plan_id,
+                                  uint32_t first_round) {
+  if (threadIdx.x == 0) { p[0] = k0; p[1] = k1; p[2] = plan_id; p[3] = first_round; }
 }
 
 }  // namespace
@@ -101,9 +105,9 @@ hipError_t launch_sample(const float* mu, const float* sigma, int n, int ha, uin
 }
 
 hipError_t launch_set_params(uint32_t* dev_params, uint64_t seed, uint32_t plan_id,
-                             hipStream_t stream) {
+                             uint32_t first_round, hipStream_t stream) {
   set_params_kernel<<<1, 64, 0, stream>>>(dev_params, (uint32_t)seed, (uint32_t)(seed >> 32),
-                                          plan_id);
+                                          plan_id, first_round);
   return hipGetLastError();
 }
 

@@ -99,6 +99,11 @@ typedef struct {
   uint32_t plan_id;    /* Philox counter word 2: distinct plans, distinct draws */
   int32_t use_graph;   /* 1: capture the R rounds once per shape as a HIP graph
                           and replay it; 0: enqueue kernels directly */
+  uint32_t first_round;   /* Philox counter word 1 of the first round (round r of
+                             this call draws with first_round + r): 0 for a fresh
+                             plan; r0 resumes a plan after r0 rounds from the mu and
+                             sigma it returned, drawing exactly what an uninterrupted
+                             plan draws in its rounds r0, r0 + 1, ... */
 } cem_params;
 
 typedef struct cem_model cem_model;   /* opaque: device weights + workspace */

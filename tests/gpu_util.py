@@ -73,7 +73,7 @@ def release_models():
 def run_plan(name: str, *, use_graph: bool = True, rounds: int | None = None,
              n: int | None = None, k: int | None = None, seed: int | None = None,
              plan_id: int = 0, horizon: int | None = None, mu_init=None, sigma_init=None,
-             z_goal=None):
+             z_goal=None, first_round: int = 0):
     """Run cem_plan on the GPU and return outputs and the full trace as numpy.
     mu_init / sigma_init [H, A] replace the fresh Gaussian when given; z_goal [P, E]
     replaces the workload's goal embedding."""
@@ -96,7 +96,8 @@ def run_plan(name: str, *, use_graph: bool = True, rounds: int | None = None,
     best = torch.empty(1, dtype=torch.int32, device="cuda")
     model.plan(to_dev(z_obs), to_dev(z_goal), to_dev(s0), mu, sigma, action, best, n_samples=N,
                n_elites=K, rounds=R, horizon=H, seed=pc.seed if seed is None else seed,
-               plan_id=plan_id, clamp_lo=pc.clamp_lo, clamp_hi=pc.clamp_hi, use_graph=use_graph)
+               plan_id=plan_id, clamp_lo=pc.clamp_lo, clamp_hi=pc.clamp_hi, use_graph=use_graph,
+               first_round=first_round)
     tr = {
         "x": model.trace(_lib.TRACE_ACTIONS, torch.empty((R, N, H, A), dtype=torch.float32, device="cuda")),
         "energy": model.trace(_lib.TRACE_ENERGY, torch.empty((R, N), dtype=torch.float32, device="cuda")),

@@ -198,3 +198,28 @@ def test_fp8_models_need_d_model_multiple_of_512(lib):
     fake = ctypes.c_void_p(0x1000)
     assert lib.cem_fp8_quantize_rows(fake, 4, 12, fake, fake, None) == -2
     assert lib.cem_fp8_quantize_rows(None, 4, 16, fake, fake, None) == -1
+
+
+def test_binding_structs_match_the_header_layout(tmp_path):
+    """The ctypes mirrors of cem_params and cem_model_desc have the size and field
+    offsets the C compiler gives the header's structs."""
+    structs = {"cem_params": _lib.Params, "cem_model_desc": _lib.ModelDesc}
+    lines = ['#include "cem_jepa.h"', "#include <stddef.h>", "#include <stdio.h>", "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for field, _ in py._fields_:
+            lines.append(f'  printf("{cname} {field} %zu\\n", offsetof({cname}, {field}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), str(src), "-o", str(exe)],
+                   check=True)
+    got = {}
+    for line in subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines():
+        cname, field, value = line.split()
+        got[(cname, field)] = int(value)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for field, _ in py._fields_:
+            assert got[(cname, field)] == getattr(py, field).offset, (cname, field)

@@ -92,9 +92,10 @@ def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
             assert r >= 0.9999
 
 
-def _lockstep(name, out, oracle_rows, mu_init=None, sigma_init=None, plan_id=None, problem=None):
+def _lockstep(name, out, oracle_rows, mu_init=None, sigma_init=None, plan_id=None, problem=None,
+              round0=0):
     """Follow the GPU plan round by round with the oracle.  problem = (z_obs, z_goal,
-    s0) replaces the workload's own inputs."""
+    s0) replaces the workload's own inputs; round0 is the plan's first Philox round."""
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
     if problem is not None:
         z_obs, z_goal, s0 = problem
@@ -108,7 +109,7 @@ def _lockstep(name, out, oracle_rows, mu_init=None, sigma_init=None, plan_id=Non
     pid = pc.plan_id if plan_id is None else plan_id
     worst = 0.0
     for r in range(R):
-        x = o_sampler.sample_actions(mu, sigma, pc.seed, r, pid, N, pc.clamp_lo, pc.clamp_hi)
+        x = o_sampler.sample_actions(mu, sigma, pc.seed, round0 + r, pid, N, pc.clamp_lo, pc.clamp_hi)
         # samples: identical up to a float32 ulp where float64 libms differ
         ulps = np.abs(out["x"][r].view(np.int32).astype(np.int64) - x.view(np.int32).astype(np.int64))
         assert ulps.max() <= 1, f"round {r}: samples differ by {ulps.max()} ulp"
@@ -274,6 +275,32 @@ def test_warm_started_closed_loop_lockstep(gpu_lib, floor):
         np.testing.assert_array_equal(to_np(mt), mu)
         np.testing.assert_array_equal(to_np(st), sigma)
         np.testing.assert_array_equal(mu[0], out["mu_out"][1])
+
+
+@pytest.mark.parametrize("name,use_graph", [("tiny", True), ("small", False), ("small", True)])
+def test_plan_resume_equals_uninterrupted(gpu_lib, name, use_graph):
+    """A plan stopped after r0 rounds and resumed from the Gaussian it returned, with
+    first_round = r0, is the uninterrupted plan bit for bit, trace included; the
+    resumed rounds also follow the oracle from that Gaussian at Philox rounds r0, ..."""
+    R, r0 = 4, 2
+    log(f"resume {name}: {r0} + {R - r0} rounds against {R}, graph={use_graph}")
+    full = run_plan(name, rounds=R, use_graph=use_graph)
+    first = run_plan(name, rounds=r0, use_graph=use_graph)
+    rest = run_plan(name, rounds=R - r0, use_graph=use_graph, mu_init=first["mu_out"],
+                    sigma_init=first["sigma_out"], first_round=r0)
+    for key in ("x", "energy", "elites"):
+        np.testing.assert_array_equal(first[key], full[key][:r0], err_msg=key)
+        np.testing.assert_array_equal(rest[key], full[key][r0:], err_msg=key)
+    for key in ("mu", "sigma"):
+        np.testing.assert_array_equal(first[key], full[key][:r0 + 1], err_msg=key)
+        np.testing.assert_array_equal(rest[key], full[key][r0:], err_msg=key)
+    for key in ("action", "mu_out", "sigma_out"):
+        np.testing.assert_array_equal(rest[key], full[key], err_msg=key)
+    assert rest["best"] == full["best"]
+    rows = (lambda r, n: np.arange(n)) if name == "tiny" else (
+        lambda r, n: np.random.default_rng(50 + r).choice(n, 6, replace=False))
+    worst = _lockstep(name, rest, rows, mu_init=first["mu_out"], sigma_init=first["sigma_out"], round0=r0)
+    log(f"  resumed rounds in lockstep with the oracle, worst energy rel err {worst:.3e}")
 
 
 def _problems(name, batch, horizon=None):
