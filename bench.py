@@ -47,11 +47,10 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0    # MI355X dense fp8
 # each scaled by what the same counter reads for a 1 GiB device copy
 # (`bench.py --copy-bytes 1073741824`): FETCH_SIZE x 2.0, WRITE_SIZE x 1.0.
 # Valid only for the GEMM sources they were taken on (sha256 below); reported
-# as null once those change.  (Taken at sha256 5e982de4...; the sources changed
-# since only in a host-side launcher check, not in device code.)
+# as null once those change.
 GEMM_COUNTERS = {
     "sources_sha256": "b906aec90b033743e46b254b684258b3272ca8a7081afd5b9e100b824296d042",
-    "bytes_per_launch": 3442020967,
+    "bytes_per_launch": 3434899121,
 }
 GEMM_SOURCES = ("cem_jepa_predictor_amd/csrc/gemm.hip", "cem_jepa_predictor_amd/csrc/common.hpp")
 
