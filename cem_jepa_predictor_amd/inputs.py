@@ -115,6 +115,12 @@ WORKLOADS: Dict[str, Workload] = {
     # from the output projection's epilogue in 32 pieces per row.
     "wide2048": Workload("wide2048", ModelConfig("wide2048", 1, 2048, 32, 2048, 16, 64, "bf16", 1),
                          PlanConfig(16, 4, 2, 1)),
+    # The V-JEPA2-AC frame-block length (256 patches, B = 258: 17 query tiles, the last
+    # holding 2 rows) on a two-layer, two-head model the oracle runs in seconds, with up
+    # to 320 candidates: the attention at that block length in both of its input modes
+    # (layer 0 reads the compact layer-0 block, layer 1 the full rows).
+    "p256": Workload("p256", ModelConfig("p256", 2, 128, 2, 256, 256, 128, "bf16", 1),
+                     PlanConfig(320, 32, 2, 1)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
     # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.

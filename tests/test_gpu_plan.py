@@ -56,7 +56,7 @@ def gpu_rollout(name, actions):
                                             ("small", 3, 1), ("oddk", 9, None), ("oddk", 9, 1),
                                             ("small_fp8", 12, None), ("small_fp8", 12, 1),
                                             ("wide768", 12, None),
-                                            ("wide2048", 9, None)])
+                                            ("wide2048", 9, None), ("p256", 16, None), ("p256", 300, None)])
 def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
     from cem_jepa_predictor_amd import inputs
 
@@ -199,23 +199,24 @@ def test_plan_graph_equals_eager_and_is_deterministic(gpu_lib, name):
     assert not np.array_equal(a["x"], d["x"])
 
 
-@pytest.mark.parametrize("horizon", [None, 1])
-def test_rollout_is_invariant_to_candidate_chunking(gpu_lib, horizon):
+@pytest.mark.parametrize("name,horizon,n,chunk", [("small", None, 64, 16), ("small", 1, 64, 16),
+                                                   ("p256", None, 300, 100)])
+def test_rollout_is_invariant_to_candidate_chunking(gpu_lib, name, horizon, n, chunk):
     """Same seeds give the same answer however candidates are grouped (cf. plans identical
     at 1, 2, 4 and 8 GPUs).  At horizon 1 the groups also change the compact layer-0 block
-    (shared rows once, then each group's action rows)."""
+    (shared rows once, then each group's action rows); p256 runs the V-JEPA2-AC block
+    length (B = 258) with 600 and 200 (candidate, head) attention items per launch."""
     import torch
     from cem_jepa_predictor_amd import _lib
 
-    name = "small"
     wl, _, _, z_obs, z_goal, s0 = workload_data(name)
     from cem_jepa_predictor_amd import inputs
 
-    actions = inputs.make_actions(64, horizon or wl.plan.horizon, seed=11)
+    actions = inputs.make_actions(n, horizon or wl.plan.horizon, seed=11)
     full = gpu_rollout(name, actions)
-    parts = np.concatenate([gpu_rollout(name, actions[i:i + 16]) for i in range(0, 64, 16)])
+    parts = np.concatenate([gpu_rollout(name, actions[i:i + chunk]) for i in range(0, n, chunk)])
     np.testing.assert_array_equal(full, parts)
-    e = torch.empty(64, dtype=torch.float32, device="cuda")
+    e = torch.empty(n, dtype=torch.float32, device="cuda")
     _lib.energy_l1(to_dev(full).to(torch.bfloat16), to_dev(z_goal), e)
     torch.cuda.synchronize()
 
