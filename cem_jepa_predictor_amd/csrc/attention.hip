@@ -34,6 +34,10 @@
 // Several frame blocks (KV cache, horizon > 1): the same 512-thread structure
 // with the blocks streamed through LDS one at a time and, per query tile, the
 // online-softmax state carried across blocks in registers.
+//
+// Layer 0 of the first frame block at horizon 1 reads q, k and v through a row
+// index instead (AttnArgs::qkv_c): each candidate's action row and its problem's
+// shared state and frame rows, projected once each into one compact block.
 #include <type_traits>
 #include <utility>
 
