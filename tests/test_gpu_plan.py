@@ -53,7 +53,7 @@ def gpu_rollout(name, actions):
 # and the candidates' action rows once, in one compact block the attention reads from.
 @pytest.mark.parametrize("name,n,horizon", [("tiny", 64, None), ("tiny", 5, None), ("small", 12, None),
                                             ("small", 3, None), ("small", 5, None), ("small", 12, 1),
-                                            ("small", 3, 1), ("oddk", 9, None), ("oddk", 9, 1),
+                                            ("small", 3, 1), ("small", 1, 1), ("oddk", 9, None), ("oddk", 9, 1),
                                             ("small_fp8", 12, None), ("small_fp8", 12, 1),
                                             ("wide768", 12, None),
                                             ("wide2048", 9, None), ("p256", 16, None), ("p256", 300, None)])
