@@ -121,6 +121,11 @@ WORKLOADS: Dict[str, Workload] = {
     # (layer 0 reads the compact layer-0 block, layer 1 the full rows).
     "p256": Workload("p256", ModelConfig("p256", 2, 128, 2, 256, 256, 128, "bf16", 1),
                      PlanConfig(320, 32, 2, 1)),
+    # 140 patches (B = 142: 9 query tiles over the attention workgroup's eight waves, the
+    # ninth holding 14 rows), horizon 2 so the second frame block runs the cached-keys
+    # kernel at that length too.
+    "p140": Workload("p140", ModelConfig("p140", 2, 128, 2, 256, 140, 128, "bf16", 2),
+                     PlanConfig(64, 8, 2, 2)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
     # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.

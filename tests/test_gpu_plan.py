@@ -50,13 +50,16 @@ def gpu_rollout(name, actions):
 # wide2048: the LayerNorm statistics of d = 768 and 2048 rows in 12 and 32 pieces (small: 8, the
 # V-JEPA2-AC shape: 16, oddk: a statistics pass of its own).  Horizon 1 on the bf16 and fp8
 # models (small, oddk, small_fp8, wide2048): layer 0 projects each problem's shared rows once
-# and the candidates' action rows once, in one compact block the attention reads from.
+# and the candidates' action rows once, in one compact block the attention reads from.  p256
+# (17 query tiles) and p140 (9): one wave of the attention workgroup takes a third (second)
+# query tile, the last, with 2 (14) rows.
 @pytest.mark.parametrize("name,n,horizon", [("tiny", 64, None), ("tiny", 5, None), ("small", 12, None),
                                             ("small", 3, None), ("small", 5, None), ("small", 12, 1),
                                             ("small", 3, 1), ("small", 1, 1), ("oddk", 9, None), ("oddk", 9, 1),
                                             ("small_fp8", 12, None), ("small_fp8", 12, 1),
                                             ("wide768", 12, None),
-                                            ("wide2048", 9, None), ("p256", 16, None), ("p256", 300, None)])
+                                            ("wide2048", 9, None), ("p256", 16, None), ("p256", 300, None),
+                                            ("p256", 5, None), ("p140", 16, None), ("p140", 40, 1)])
 def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
     from cem_jepa_predictor_amd import inputs
 
@@ -200,7 +203,7 @@ def test_plan_graph_equals_eager_and_is_deterministic(gpu_lib, name):
 
 
 @pytest.mark.parametrize("name,horizon,n,chunk", [("small", None, 64, 16), ("small", 1, 64, 16),
-                                                   ("p256", None, 300, 100)])
+                                                   ("p256", None, 300, 100), ("p140", None, 64, 24)])
 def test_rollout_is_invariant_to_candidate_chunking(gpu_lib, name, horizon, n, chunk):
     """Same seeds give the same answer however candidates are grouped (cf. plans identical
     at 1, 2, 4 and 8 GPUs).  At horizon 1 the groups also change the compact layer-0 block
