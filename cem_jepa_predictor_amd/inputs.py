@@ -126,6 +126,10 @@ WORKLOADS: Dict[str, Workload] = {
     # kernel at that length too.
     "p140": Workload("p140", ModelConfig("p140", 2, 128, 2, 256, 140, 128, "bf16", 2),
                      PlanConfig(64, 8, 2, 2)),
+    # The longest frame block the bf16 attention takes: 318 patches, B = 320 (20 query and
+    # key tiles, K and V of a block filling half of a CU's LDS), horizon 2.
+    "p318": Workload("p318", ModelConfig("p318", 2, 128, 2, 256, 318, 128, "bf16", 2),
+                     PlanConfig(64, 8, 2, 2)),
     # V-JEPA2-AC-shaped predictor, horizon 1: the measured plan step.
     "vjepa2ac": Workload("vjepa2ac", _vj("vjepa2ac", 1, 1), PlanConfig(800, 80, 10, 1)),
     # Same predictor and search with the fp8 (e4m3) q|k|v and MLP-up projections.

@@ -52,14 +52,15 @@ def gpu_rollout(name, actions):
 # models (small, oddk, small_fp8, wide2048): layer 0 projects each problem's shared rows once
 # and the candidates' action rows once, in one compact block the attention reads from.  p256
 # (17 query tiles) and p140 (9): one wave of the attention workgroup takes a third (second)
-# query tile, the last, with 2 (14) rows.
+# query tile, the last, with 2 (14) rows.  p318: the longest block (B = 320, 20 tiles).
 @pytest.mark.parametrize("name,n,horizon", [("tiny", 64, None), ("tiny", 5, None), ("small", 12, None),
                                             ("small", 3, None), ("small", 5, None), ("small", 12, 1),
                                             ("small", 3, 1), ("small", 1, 1), ("oddk", 9, None), ("oddk", 9, 1),
                                             ("small_fp8", 12, None), ("small_fp8", 12, 1),
                                             ("wide768", 12, None),
                                             ("wide2048", 9, None), ("p256", 16, None), ("p256", 300, None),
-                                            ("p256", 5, None), ("p140", 16, None), ("p140", 40, 1)])
+                                            ("p256", 5, None), ("p140", 16, None), ("p140", 40, 1),
+                                            ("p318", 16, None), ("p318", 24, 1)])
 def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
     from cem_jepa_predictor_amd import inputs
 
@@ -590,3 +591,23 @@ def test_plan_small_reachable_goal_independent(gpu_lib):
         f"(a* first step {np.round(a_star[0, 0], 3).tolist()}): max diff {diff:.3f}; round-0 elites shared {shared0}/32")
     assert shared0 >= 28
     assert diff <= 0.15
+
+
+@pytest.mark.parametrize("d_model,patches,heads,dtype,msg", [(128, 319, 2, "bf16", "patches + 2 <= 320"),
+                                                             (128, 318, 4, "bf16", "head dim 64"),
+                                                             (512, 319, 8, "fp8", "patches + 2 <= 320"),
+                                                             (128, 318, 2, "fp8", "d_model % 512")])
+def test_model_create_rejects_shapes_beyond_the_attention(gpu_lib, d_model, patches, heads, dtype, msg):
+    """One past the longest frame block (B = 321), a head dim other than 64, or an fp8 width
+    that is not a multiple of 512 is refused at creation with a shape error, not launched."""
+    import dataclasses
+
+    from cem_jepa_predictor_amd import _lib, inputs
+
+    cfg = dataclasses.replace(inputs.WORKLOADS["p318"].model, name="reject", d_model=d_model,
+                              patches=patches, heads=heads, dtype=dtype)
+    flat = inputs.flatten_weights(cfg, inputs.make_weights(cfg, 0))
+    with pytest.raises(_lib.CemError) as e:
+        _lib.Model(cfg, flat, 8)
+    log(f"  {cfg.patches} patches, {cfg.heads} heads, {dtype}: {e.value}")
+    assert msg in str(e.value)
