@@ -126,6 +126,10 @@ WORKLOADS: Dict[str, Workload] = {
     # kernel at that length too.
     "p140": Workload("p140", ModelConfig("p140", 2, 128, 2, 256, 140, 128, "bf16", 2),
                      PlanConfig(64, 8, 2, 2)),
+    # One bf16 layer at the widest d_model the library takes (4096, 64 heads): statistics
+    # in 64 pieces per row, K = 4096 in every projection.
+    "wide4096": Workload("wide4096", ModelConfig("wide4096", 1, 4096, 64, 4096, 16, 64, "bf16", 1),
+                         PlanConfig(16, 4, 2, 1)),
     # The longest frame block the bf16 attention takes: 318 patches, B = 320 (20 query and
     # key tiles, K and V of a block filling half of a CU's LDS), horizon 2.
     "p318": Workload("p318", ModelConfig("p318", 2, 128, 2, 256, 318, 128, "bf16", 2),

@@ -53,6 +53,7 @@ def gpu_rollout(name, actions):
 # and the candidates' action rows once, in one compact block the attention reads from.  p256
 # (17 query tiles) and p140 (9): one wave of the attention workgroup takes a third (second)
 # query tile, the last, with 2 (14) rows.  p318: the longest block (B = 320, 20 tiles).
+# wide4096: the widest model (d = 4096, 64 statistics pieces per row).
 @pytest.mark.parametrize("name,n,horizon", [("tiny", 64, None), ("tiny", 5, None), ("small", 12, None),
                                             ("small", 3, None), ("small", 5, None), ("small", 12, 1),
                                             ("small", 3, 1), ("small", 1, 1), ("oddk", 9, None), ("oddk", 9, 1),
@@ -60,7 +61,7 @@ def gpu_rollout(name, actions):
                                             ("wide768", 12, None),
                                             ("wide2048", 9, None), ("p256", 16, None), ("p256", 300, None),
                                             ("p256", 5, None), ("p140", 16, None), ("p140", 40, 1),
-                                            ("p318", 16, None), ("p318", 24, 1)])
+                                            ("p318", 16, None), ("p318", 24, 1), ("wide4096", 5, None)])
 def test_rollout_matches_oracle(gpu_lib, name, n, horizon):
     from cem_jepa_predictor_amd import inputs
 
